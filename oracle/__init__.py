@@ -1,0 +1,16 @@
+"""CPU oracle for the paged KV-cache hot path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import or run anything in this
+package.  The product path (the HIP library and its Python binding) never
+imports it, and this package never imports the product path.
+
+``ref``   numpy fp64 definitions of the three operations (store, decode,
+          varlen causal prefill) and of the split-K partials and merge.
+``brute`` pure-Python loop versions of decode and prefill for tiny inputs,
+          written independently of ``ref`` to pin it.
+
+Parity status: every function here is pinned by CPU tests (brute force,
+library SDPA on contiguous tensors, closed forms, invariants and the worked
+address-translation example printed on the pages); none is "parity unpinned".
+"""

@@ -1,0 +1,71 @@
+"""Pure-Python loop versions of paged decode and prefill for tiny inputs.
+
+TEST INFRASTRUCTURE ONLY.  Written independently of ``oracle.ref`` (no shared
+helpers) so that it can pin it: every key is fetched cell by cell through the
+block table with the page/offset translation of the vLLM essay (lshu.cn,
+section 3.2), every dot product and exponential is a scalar loop.
+
+Inputs are nested Python lists (or anything indexable) of floats:
+q[b][h][d], cache[p][g][o][d], block_tables[b][i], context_lens[b].
+"""
+
+import math
+
+
+def _key(cache, table, j, g, B):
+    page = table[j // B]
+    return cache[page][g][j % B]
+
+
+def _attend_one(qv, cache_k, cache_v, table, nkeys, g, B, scale):
+    D = len(qv)
+    if nkeys <= 0:
+        return [0.0] * D
+    scores = []
+    for j in range(nkeys):
+        kr = _key(cache_k, table, j, g, B)
+        s = 0.0
+        for d in range(D):
+            s += qv[d] * kr[d]
+        scores.append(s * scale)
+    top = max(scores)
+    ex = [math.exp(s - top) for s in scores]
+    tot = math.fsum(ex)
+    out = [0.0] * D
+    for j in range(nkeys):
+        vr = _key(cache_v, table, j, g, B)
+        w = ex[j] / tot
+        for d in range(D):
+            out[d] += w * vr[d]
+    return out
+
+
+def decode(q, cache_k, cache_v, block_tables, context_lens, scale, num_kv_heads, block_size):
+    out = []
+    for b in range(len(context_lens)):
+        hq = len(q[b])
+        group = hq // num_kv_heads
+        row = []
+        for h in range(hq):
+            row.append(_attend_one(q[b][h], cache_k, cache_v, block_tables[b],
+                                   context_lens[b], h // group, block_size, scale))
+        out.append(row)
+    return out
+
+
+def prefill(q, cache_k, cache_v, cu_seqlens_q, context_lens, block_tables, scale,
+            num_kv_heads, block_size):
+    out = [None] * len(q)
+    for b in range(len(context_lens)):
+        start, stop = cu_seqlens_q[b], cu_seqlens_q[b + 1]
+        n_q, n_k = stop - start, context_lens[b]
+        for i in range(n_q):
+            pos = n_k - n_q + i  # position of this query in its sequence
+            hq = len(q[start + i])
+            group = hq // num_kv_heads
+            out[start + i] = [
+                _attend_one(q[start + i][h], cache_k, cache_v, block_tables[b],
+                            pos + 1, h // group, block_size, scale)
+                for h in range(hq)
+            ]
+    return out
