@@ -1,0 +1,219 @@
+/*
+ * pkv.h -- C ABI of the paged KV-cache attention library (libpkv.so), gfx950.
+ *
+ * The library implements the per-layer hot path of a block-table KV cache as
+ * the nano-vllm pages describe it:
+ *   - nano-vllm source study (hk.pswp.cn), section 2 "注意力層": the attention
+ *     layer first stores the fresh k/v rows into the cache at slot_mapping (a
+ *     store kernel), then runs varlen attention with prefix cache in prefill
+ *     and attention over the paged cache in decode;
+ *   - nano-vllm architecture page (repothread.com), "Dynamische
+ *     KV-Cache-Allokation" (cache indexed by block, row, kv head, head dim),
+ *     "Prefill- und Decode-Vorbereitung" (slot = block id * block size + row;
+ *     uncached positions run from the cached prefix length to the sequence
+ *     length), "Kern-Designentscheidungen" item 1 (256-token blocks);
+ *   - vLLM essay (lshu.cn), section 3.2: logical position -> (block index =
+ *     pos / block size, row = pos % block size), then gather and compute.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * Pointers named "device" point to device memory (HBM) of the current HIP
+ * device; host scalars are passed by value.  The caller owns every buffer;
+ * the library never allocates, frees or synchronises.  Work is enqueued on
+ * `stream` (a hipStream_t; NULL = the null stream) in stream order and runs
+ * asynchronously; a PKV_OK return means the launch was enqueued.
+ *
+ * Element types: PKV_FP32 (float) or PKV_BF16 (bfloat16 bit patterns, uint16
+ * storage).  Index arrays are int32.  Every value pointer must be 16-byte
+ * aligned and every token stride must keep rows 16-byte aligned.
+ *
+ * KV cache layout of one layer (one tensor for K, one for V):
+ *     cache[num_blocks][num_kv_heads][block_size][head_dim], dense, row-major;
+ * element (p, g, o, d) is at ((p * num_kv_heads + g) * block_size + o) *
+ * head_dim + d.  Physical slot s means block s / block_size, row
+ * s % block_size.  This keeps the rows of one (block, kv head) contiguous.
+ * block_size must be 256 and head_dim 128.
+ *
+ * GQA: query head h reads kv head h / (num_q_heads / num_kv_heads).
+ * Attention: out = sum_j softmax_j(scale * q . k_j) v_j over the visible keys,
+ * fp32 accumulation, output in the input element type (bf16 rounded to
+ * nearest even).  A query with no visible key gets a zero output row.
+ *
+ * Errors: host scalars and pointers are checked before any HIP call.
+ *   PKV_ERR_INVALID      null pointer with a non-zero count, a count or size
+ *                        < 0 (or <= 0 where a size must be positive),
+ *                        num_q_heads % num_kv_heads != 0, misalignment,
+ *                        max_context_len > max_blocks_per_seq * block_size,
+ *                        causal != 1;
+ *   PKV_ERR_UNSUPPORTED  block_size != 256, head_dim != 128, a GQA group size
+ *                        not in {1, 2, 4, 8} and not a multiple of 8, fp32
+ *                        prefill;
+ *   PKV_ERR_WORKSPACE    decode workspace smaller than required;
+ *   PKV_ERR_HIP          a HIP launch reported an error.
+ * A zero count (no tokens, empty batch) returns PKV_OK and launches nothing.
+ * Device array *contents* are not checked: a slot outside [-1,
+ * num_blocks * block_size), a block id outside [0, num_blocks) in a used
+ * table column, context_lens[b] > max_context_len, or cu_seqlens_q that is not
+ * non-decreasing are undefined behaviour.  pkv_last_error() describes the
+ * most recent non-OK status of the calling thread.
+ *
+ * Results are deterministic: a pure function of the inputs and the split
+ * plan; no reduction uses atomics.
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID = 1,
+  PKV_ERR_UNSUPPORTED = 2,
+  PKV_ERR_WORKSPACE = 3,
+  PKV_ERR_HIP = 4
+} pkv_status;
+
+typedef enum { PKV_FP32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+/*
+ * pkv_kv_store -- slot scatter of this step's K and V rows into the cache
+ * (source study section 2, the store kernel; architecture page "Prefill- und
+ * Decode-Vorbereitung" for the slots).
+ *
+ *   k, v            device, [num_tokens][num_kv_heads][head_dim]; token t's
+ *                   row starts at t * k_token_stride (v_token_stride)
+ *                   elements, heads are head_dim apart (so k and v may be
+ *                   views into a fused qkv tensor)
+ *   k_cache,v_cache device, cache layout above, num_blocks blocks; written
+ *   slot_mapping    device int32 [num_tokens]; token t goes to slot
+ *                   slot_mapping[t] for every kv head; -1 stores nothing
+ *
+ * Pure bitwise copy (no conversion); cells not addressed by a slot are left
+ * unchanged.  Two tokens with the same slot are undefined behaviour.
+ */
+pkv_status pkv_kv_store(pkv_dtype dtype, const void* k, int64_t k_token_stride,
+                        const void* v, int64_t v_token_stride, void* k_cache,
+                        void* v_cache, const int32_t* slot_mapping,
+                        int32_t num_tokens, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size,
+                        int64_t num_blocks, void* stream);
+
+/*
+ * pkv_paged_decode_workspace_bytes -- bytes of fp32 workspace that
+ * pkv_paged_decode needs for the split-K partials with the same arguments
+ * (0 when the plan uses a single split).  num_splits: 0 = automatic, else the
+ * number of splits of max_context_len requested.  Returns 0 for invalid or
+ * unsupported arguments (pkv_paged_decode then reports the error).
+ */
+size_t pkv_paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t max_context_len,
+                                        int32_t block_size, int32_t num_splits);
+
+/*
+ * pkv_paged_decode_split_tokens -- keys per split that pkv_paged_decode uses
+ * with these arguments (a multiple of 64; >= max_context_len means one
+ * split).  Returns 0 for invalid or unsupported arguments.
+ */
+int32_t pkv_paged_decode_split_tokens(int32_t batch, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t max_context_len,
+                                      int32_t block_size, int32_t num_splits);
+
+/*
+ * pkv_paged_decode -- one query token per sequence attends its whole context
+ * gathered through its block table (source study section 2, decode attention
+ * with the KV cache; essay section 3.2, gather then compute).  Long contexts
+ * are split into chunks of S keys (flash-decoding split-K); the partials are
+ * merged in split order.
+ *
+ *   q              device, [batch][num_q_heads][head_dim]; sequence b's row
+ *                  starts at b * q_token_stride elements, heads head_dim apart
+ *   k_cache,v_cache device, cache layout above (read only)
+ *   block_tables   device int32 [batch][max_blocks_per_seq]; column i of row
+ *                  b is the physical block of logical block i; columns
+ *                  >= ceil(context_lens[b] / block_size) are never read
+ *   context_lens   device int32 [batch]; keys of sequence b, including the
+ *                  token stored this step (the query sits at position
+ *                  context_lens[b] - 1); 0 gives a zero output row
+ *   max_context_len host; >= every context_lens[b]; sets the split plan
+ *   scale          softmax scale (e.g. 1/sqrt(head_dim))
+ *   num_splits     0 = automatic; otherwise the requested number of splits
+ *   out            device, [batch][num_q_heads][head_dim], dense, dtype
+ *   workspace      device, >= pkv_paged_decode_workspace_bytes(...) bytes,
+ *                  16-byte aligned, may be NULL when that is 0.  Layout:
+ *                  float acc[batch][num_q_heads][nsplit][head_dim] followed
+ *                  by float ml[batch][num_q_heads][nsplit][2], nsplit =
+ *                  ceil(max_context_len / S).  For split s of sequence b
+ *                  (keys s*S .. min(n,(s+1)*S)-1) with x_j = scale*q.k_j and
+ *                  splits that exist (s*S < n): ml = (m, l) where m =
+ *                  max_j x_j * log2(e) and l = sum_j 2^(x_j*log2(e) - m), and
+ *                  acc = sum_j 2^(x_j*log2(e) - m) v_j.  Sequences with a
+ *                  single split do not use their slots.
+ */
+pkv_status pkv_paged_decode(pkv_dtype dtype, const void* q,
+                            int64_t q_token_stride, const void* k_cache,
+                            const void* v_cache, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq,
+                            const int32_t* context_lens,
+                            int32_t max_context_len, int32_t batch,
+                            int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size,
+                            int64_t num_blocks, float scale, int32_t num_splits,
+                            void* out, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
+ * pkv_paged_prefill_varlen -- varlen causal prefill whose keys come from the
+ * cache through the block table, including prefix blocks cached (and shared)
+ * before this step (source study section 2, varlen attention with prefix
+ * cache; architecture page "Prefill- und Decode-Vorbereitung" and
+ * "Hash-basiertes Prefix Caching").  bf16 only.
+ *
+ *   q              device, packed [total_q][num_q_heads][head_dim]; query row
+ *                  r starts at r * q_token_stride elements
+ *   cu_seqlens_q   device int32 [batch + 1]; sequence b owns query rows
+ *                  cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (n_q of them)
+ *   max_seqlen_q   host; >= every n_q
+ *   context_lens   device int32 [batch]; n_k, keys of sequence b after this
+ *                  step's store (cached prefix plus the n_q new tokens)
+ *   max_context_len host; >= every n_k
+ *   block_tables   as for decode
+ *   causal         must be 1: query i of sequence b sits at position
+ *                  n_k - n_q + i and sees keys 0 .. n_k - n_q + i
+ *   out            device, [total_q][num_q_heads][head_dim], dense, bf16
+ * total_q = cu_seqlens_q[batch] is not passed; rows outside the ranges are
+ * neither read nor written.
+ */
+pkv_status pkv_paged_prefill_varlen(
+    pkv_dtype dtype, const void* q, int64_t q_token_stride,
+    const void* k_cache, const void* v_cache, const int32_t* cu_seqlens_q,
+    int32_t max_seqlen_q, const int32_t* context_lens, int32_t max_context_len,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t batch,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int64_t num_blocks, float scale, int32_t causal,
+    void* out, void* stream);
+
+/*
+ * pkv_kv_block_bytes -- bytes of one block of one of K or V for one layer
+ * (block_size * num_kv_heads * head_dim * element size); the pages size the
+ * cache as a whole number of such blocks ("Dynamische KV-Cache-Allokation").
+ * Returns -1 for invalid arguments.
+ */
+int64_t pkv_kv_block_bytes(pkv_dtype dtype, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size);
+
+/* pkv_last_error -- message for the calling thread's last non-OK status
+ * ("" if none).  The string is owned by the library. */
+const char* pkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

@@ -1,0 +1,250 @@
+// C ABI of libpkv: argument checks, split planning and kernel launches.
+// Every check on host scalars and pointers happens before the first HIP call.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/pkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pkv_status fail(pkv_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+pkv_status fail(pkv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+pkv_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PKV_OK;
+  return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(pkv_dtype dt) { return dt == PKV_BF16 ? 2 : dt == PKV_FP32 ? 4 : 0; }
+
+// Checks shared by the three attention-side entry points.
+pkv_status check_geometry(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size) {
+  if (num_q_heads <= 0 || num_kv_heads <= 0)
+    return fail(PKV_ERR_INVALID, "num_q_heads (%d) and num_kv_heads (%d) must be positive",
+                num_q_heads, num_kv_heads);
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                num_q_heads, num_kv_heads);
+  if (head_dim <= 0 || block_size <= 0)
+    return fail(PKV_ERR_INVALID, "head_dim (%d) and block_size (%d) must be positive", head_dim,
+                block_size);
+  if (head_dim != pkv::kHeadDim)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d is not supported (only 128)", head_dim);
+  if (block_size != pkv::kBlockSize)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size %d is not supported (only 256)", block_size);
+  return PKV_OK;
+}
+
+pkv_status check_stride(const char* name, int64_t stride, int64_t min_elems, int eb) {
+  if (stride < min_elems)
+    return fail(PKV_ERR_INVALID, "%s (%lld) is smaller than a row (%lld elements)", name,
+                (long long)stride, (long long)min_elems);
+  if ((stride * eb) % 16 != 0)
+    return fail(PKV_ERR_INVALID, "%s (%lld elements) does not keep rows 16-byte aligned", name,
+                (long long)stride);
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+int64_t pkv_kv_block_bytes(pkv_dtype dtype, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size) {
+  const int eb = elem_bytes(dtype);
+  if (eb == 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0) return -1;
+  return (int64_t)block_size * num_kv_heads * head_dim * eb;
+}
+
+pkv_status pkv_kv_store(pkv_dtype dtype, const void* k, int64_t k_token_stride, const void* v,
+                        int64_t v_token_stride, void* k_cache, void* v_cache,
+                        const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size, int64_t num_blocks, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (eb == 0) return fail(PKV_ERR_INVALID, "unknown dtype %d", (int)dtype);
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID, "num_tokens (%d) < 0", num_tokens);
+  if (num_blocks < 0) return fail(PKV_ERR_INVALID, "num_blocks (%lld) < 0", (long long)num_blocks);
+  pkv_status st = check_geometry(num_kv_heads, num_kv_heads, head_dim, block_size);
+  if (st != PKV_OK) return st;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping)
+    return fail(PKV_ERR_INVALID, "null pointer argument with num_tokens = %d", num_tokens);
+  if (num_blocks == 0)
+    return fail(PKV_ERR_INVALID, "num_blocks is 0 but %d tokens are to be stored", num_tokens);
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_ERR_INVALID, "k, v, k_cache and v_cache must be 16-byte aligned");
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if ((st = check_stride("k_token_stride", k_token_stride, row, eb)) != PKV_OK) return st;
+  if ((st = check_stride("v_token_stride", v_token_stride, row, eb)) != PKV_OK) return st;
+  if (num_blocks * block_size > (int64_t)INT32_MAX + 1)
+    return fail(PKV_ERR_UNSUPPORTED, "num_blocks * block_size exceeds the int32 slot range");
+  return hip_status(pkv::launch_kv_store(eb, k, k_token_stride, v, v_token_stride, k_cache,
+                                         v_cache, slot_mapping, num_tokens, num_kv_heads,
+                                         (hipStream_t)stream),
+                    "kv_store launch");
+}
+
+static bool decode_plan_for(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t max_context_len, int32_t block_size,
+                            int32_t num_splits, pkv::DecodePlan* plan) {
+  if (batch < 0 || max_context_len < 0 || num_splits < 0) return false;
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads) return false;
+  if (head_dim != pkv::kHeadDim || block_size != pkv::kBlockSize) return false;
+  return pkv::plan_decode(batch, num_q_heads, num_kv_heads, max_context_len, num_splits, plan);
+}
+
+size_t pkv_paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t max_context_len,
+                                        int32_t block_size, int32_t num_splits) {
+  pkv::DecodePlan plan;
+  if (!decode_plan_for(batch, num_q_heads, num_kv_heads, head_dim, max_context_len, block_size,
+                       num_splits, &plan))
+    return 0;
+  return plan.workspace_bytes;
+}
+
+int32_t pkv_paged_decode_split_tokens(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t max_context_len,
+                                      int32_t block_size, int32_t num_splits) {
+  pkv::DecodePlan plan;
+  if (!decode_plan_for(batch, num_q_heads, num_kv_heads, head_dim, max_context_len, block_size,
+                       num_splits, &plan))
+    return 0;
+  return plan.split_tokens;
+}
+
+pkv_status pkv_paged_decode(pkv_dtype dtype, const void* q, int64_t q_token_stride,
+                            const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t max_context_len, int32_t batch,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int64_t num_blocks, float scale,
+                            int32_t num_splits, void* out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (eb == 0) return fail(PKV_ERR_INVALID, "unknown dtype %d", (int)dtype);
+  if (batch < 0) return fail(PKV_ERR_INVALID, "batch (%d) < 0", batch);
+  if (max_context_len < 0 || max_blocks_per_seq < 0 || num_blocks < 0 || num_splits < 0)
+    return fail(PKV_ERR_INVALID,
+                "max_context_len, max_blocks_per_seq, num_blocks and num_splits must be >= 0");
+  pkv_status st = check_geometry(num_q_heads, num_kv_heads, head_dim, block_size);
+  if (st != PKV_OK) return st;
+  if (pkv::decode_heads_per_wg(num_q_heads / num_kv_heads) == 0)
+    return fail(PKV_ERR_UNSUPPORTED, "GQA group size %d is not supported",
+                num_q_heads / num_kv_heads);
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(PKV_ERR_INVALID, "max_context_len (%d) > max_blocks_per_seq (%d) * block_size",
+                max_context_len, max_blocks_per_seq);
+  if (batch == 0) return PKV_OK;
+  if (!q || !context_lens || !out)
+    return fail(PKV_ERR_INVALID, "null q, context_lens or out with batch = %d", batch);
+  if (max_context_len > 0 && (!k_cache || !v_cache || !block_tables || num_blocks == 0))
+    return fail(PKV_ERR_INVALID, "null cache or block table (or no blocks) with max_context_len = %d",
+                max_context_len);
+  if (!aligned16(q) || !aligned16(out) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_ERR_INVALID, "q, out, k_cache and v_cache must be 16-byte aligned");
+  if ((st = check_stride("q_token_stride", q_token_stride, (int64_t)num_q_heads * head_dim, eb)) !=
+      PKV_OK)
+    return st;
+  if (!(scale == scale)) return fail(PKV_ERR_INVALID, "scale is NaN");
+  pkv::DecodePlan plan;
+  if (!pkv::plan_decode(batch, num_q_heads, num_kv_heads, max_context_len, num_splits, &plan))
+    return fail(PKV_ERR_UNSUPPORTED, "no decode plan for these arguments");
+  if (workspace_bytes < plan.workspace_bytes || (plan.workspace_bytes && !workspace))
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
+                workspace ? workspace_bytes : (size_t)0, plan.workspace_bytes);
+  if (plan.workspace_bytes && !aligned16(workspace))
+    return fail(PKV_ERR_INVALID, "workspace must be 16-byte aligned");
+  pkv::DecodeLaunch l;
+  l.q = q;
+  l.q_stride = q_token_stride;
+  l.k_cache = k_cache;
+  l.v_cache = v_cache;
+  l.block_tables = block_tables;
+  l.max_blocks = max_blocks_per_seq;
+  l.context_lens = context_lens;
+  l.batch = batch;
+  l.num_q_heads = num_q_heads;
+  l.num_kv_heads = num_kv_heads;
+  l.scale = scale;
+  l.out = out;
+  l.workspace = plan.workspace_bytes ? (float*)workspace : nullptr;
+  return hip_status(pkv::launch_decode(eb, plan, l, (hipStream_t)stream), "paged_decode launch");
+}
+
+pkv_status pkv_paged_prefill_varlen(pkv_dtype dtype, const void* q, int64_t q_token_stride,
+                                    const void* k_cache, const void* v_cache,
+                                    const int32_t* cu_seqlens_q, int32_t max_seqlen_q,
+                                    const int32_t* context_lens, int32_t max_context_len,
+                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                    int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                    float scale, int32_t causal, void* out, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (eb == 0) return fail(PKV_ERR_INVALID, "unknown dtype %d", (int)dtype);
+  if (batch < 0 || max_seqlen_q < 0 || max_context_len < 0 || max_blocks_per_seq < 0 ||
+      num_blocks < 0)
+    return fail(PKV_ERR_INVALID,
+                "batch, max_seqlen_q, max_context_len, max_blocks_per_seq and num_blocks must be "
+                ">= 0");
+  if (causal != 1) return fail(PKV_ERR_INVALID, "causal must be 1 (got %d)", causal);
+  pkv_status st = check_geometry(num_q_heads, num_kv_heads, head_dim, block_size);
+  if (st != PKV_OK) return st;
+  if (dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "paged_prefill_varlen supports bf16 only");
+  if (!pkv::prefill_supported_group(num_q_heads / num_kv_heads))
+    return fail(PKV_ERR_UNSUPPORTED, "GQA group size %d is not supported",
+                num_q_heads / num_kv_heads);
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(PKV_ERR_INVALID, "max_context_len (%d) > max_blocks_per_seq (%d) * block_size",
+                max_context_len, max_blocks_per_seq);
+  if (batch == 0 || max_seqlen_q == 0) return PKV_OK;
+  if (!q || !cu_seqlens_q || !context_lens || !out)
+    return fail(PKV_ERR_INVALID, "null q, cu_seqlens_q, context_lens or out");
+  if (max_context_len > 0 && (!k_cache || !v_cache || !block_tables || num_blocks == 0))
+    return fail(PKV_ERR_INVALID, "null cache or block table (or no blocks) with max_context_len = %d",
+                max_context_len);
+  if (!aligned16(q) || !aligned16(out) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_ERR_INVALID, "q, out, k_cache and v_cache must be 16-byte aligned");
+  if ((st = check_stride("q_token_stride", q_token_stride, (int64_t)num_q_heads * head_dim, eb)) !=
+      PKV_OK)
+    return st;
+  if (!(scale == scale)) return fail(PKV_ERR_INVALID, "scale is NaN");
+  pkv::PrefillLaunch l;
+  l.q = q;
+  l.q_stride = q_token_stride;
+  l.k_cache = k_cache;
+  l.v_cache = v_cache;
+  l.cu_seqlens_q = cu_seqlens_q;
+  l.max_seqlen_q = max_seqlen_q;
+  l.context_lens = context_lens;
+  l.block_tables = block_tables;
+  l.max_blocks = max_blocks_per_seq;
+  l.batch = batch;
+  l.num_q_heads = num_q_heads;
+  l.num_kv_heads = num_kv_heads;
+  l.scale = scale;
+  l.out = out;
+  return hip_status(pkv::launch_prefill(l, (hipStream_t)stream), "paged_prefill_varlen launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,404 @@
+// Paged GQA decode with split-K (flash-decoding) for gfx950.
+//
+// Operation (nano-vllm source study, section 2: decode attention over the
+// paged KV cache with per-sequence context lengths and block tables; vLLM
+// essay, section 3.2: translate logical positions to (block, row), gather,
+// compute): for sequence b and query head h, with g = h / (Hq/Hkv) and
+// n = context_lens[b],
+//     out[b][h] = sum_{j<n} softmax_j(scale * q[b][h] . K_j) V_j,
+//     K_j = k_cache[block_tables[b][j / 256]][g][j % 256].
+//
+// Work decomposition.  One workgroup is ONE wavefront and owns (split s,
+// sequence b, kv head g, chunk of heads_per_wg query heads of g's group).  It
+// walks the keys s*S .. min(n,(s+1)*S)-1 in chunks of 64 (32 for fp32)
+// tokens.  A chunk never crosses a 256-token block, and in the
+// [block][kv head][row][dim] layout its K rows (and V rows) for kv head g are
+// one contiguous 16 KiB run, read once per chunk for all heads of the group.
+//
+// Per chunk:
+//   1. K and V rows are loaded with fully coalesced 16-byte loads (each wave
+//      load instruction reads 1 KiB contiguous).  K goes to LDS with rows
+//      padded by 16 bytes.
+//   2. QK: lane t owns token t and reads its whole K row back from LDS
+//      (the padding makes 16 consecutive rows hit 16 different bank groups);
+//      q comes from LDS as a broadcast.  bf16 uses v_dot2_f32_bf16, so no
+//      conversion and no cross-lane reduction is needed for the scores.
+//   3. Online softmax in base 2 (x = scale*log2(e)*score): the chunk max is a
+//      wave reduction, p = 2^(x - m) is computed once per (token, head).
+//   4. PV: V stays in the registers it was loaded into -- lane l holds 8 (4)
+//      consecutive dims of token 4i + l/16 (2i + l/32) -- and takes p from
+//      LDS; the token groups are summed once at the end of the split.
+// Rows past the context inside the last block are read (they are inside the
+// allocation) but their score is replaced by -inf and their V by 0, so NaN
+// poison there cannot leak.
+//
+// Each split writes unnormalised (acc, m, l) to the workspace; the merge
+// kernel combines them in split order (deterministic).  A sequence with one
+// split writes its output directly.  HBM-bound: the algorithmic traffic is
+// the context's K and V bytes plus q and out.
+#include <math.h>
+
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+namespace {
+
+constexpr int kTargetWaves = 256 * 32;  // 256 CUs; enough waves for balance
+
+template <int kElemBytes>
+struct DecodeShape {
+  static constexpr int kVec = 16 / kElemBytes;            // elements per 16-byte chunk
+  static constexpr int kChunksPerRow = kHeadDim / kVec;   // 16 (bf16) or 32 (fp32)
+  static constexpr int kRowBytes = kHeadDim * kElemBytes;  // 256 or 512
+  static constexpr int kRowsPerLoad = 64 / kChunksPerRow;  // rows per wave load: 4 or 2
+  static constexpr int kTokens = (kElemBytes == 2) ? 64 : 32;  // tokens per chunk
+  static constexpr int kLoads = kTokens / kRowsPerLoad;        // 16 for both
+};
+
+struct DecodeArgs {
+  const uint8_t* q;
+  int64_t q_stride_bytes;
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  const int32_t* block_tables;
+  int32_t max_blocks;
+  const int32_t* context_lens;
+  int32_t batch, num_q_heads, num_kv_heads, group, head_chunks;
+  float scale_log2;
+  int32_t split_tokens, nsplit;
+  uint8_t* out;
+  float* ws_acc;
+  float* ws_ml;
+};
+
+template <int kElemBytes>
+__device__ __forceinline__ void unpack(const u32x4& w, float* f) {
+  if constexpr (kElemBytes == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_lo(w[i]);
+      f[2 * i + 1] = bf16_hi(w[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
+  }
+}
+
+template <int kElemBytes, int kHeads>
+__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+  using S = DecodeShape<kElemBytes>;
+  constexpr int kVec = S::kVec;
+  constexpr int kCPR = S::kChunksPerRow;
+  constexpr int kTok = S::kTokens;
+
+  // K rows padded by one 16-byte column: row stride kCPR + 1 chunks
+  __shared__ u32x4 k_lds[kTok * (kCPR + 1)];
+  __shared__ u32x4 q_lds[kHeads * kCPR];
+  __shared__ float p_lds[kTok * kHeads];
+
+  const int lane = threadIdx.x;
+  int id = blockIdx.x;
+  const int hc = id % a.head_chunks;
+  id /= a.head_chunks;
+  const int g = id % a.num_kv_heads;
+  id /= a.num_kv_heads;
+  const int b = id % a.batch;
+  const int s = id / a.batch;
+
+  const int n = a.context_lens[b];
+  const int start = s * a.split_tokens;
+  const int h0 = g * a.group + hc * kHeads;
+  if (start >= n) {
+    if (s == 0) {  // empty context: zero output rows
+      for (int i = lane; i < kHeads * kCPR; i += 64) {
+        const int h = i / kCPR, c = i % kCPR;
+        uint8_t* o = a.out + ((int64_t)b * a.num_q_heads + h0 + h) * S::kRowBytes + c * 16;
+        *reinterpret_cast<u32x4*>(o) = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    return;
+  }
+  const int end = min(n, start + a.split_tokens);
+  const int nsplit_b = (n + a.split_tokens - 1) / a.split_tokens;
+
+  // query rows of the heads handled here -> LDS
+  for (int i = lane; i < kHeads * kCPR; i += 64) {
+    const int h = i / kCPR, c = i % kCPR;
+    q_lds[i] = *reinterpret_cast<const u32x4*>(a.q + b * a.q_stride_bytes +
+                                                (int64_t)(h0 + h) * S::kRowBytes + c * 16);
+  }
+
+  float m[kHeads], lsum[kHeads], acc[kHeads][kVec];
+#pragma unroll
+  for (int h = 0; h < kHeads; ++h) {
+    m[h] = -INFINITY;
+    lsum[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) acc[h][e] = 0.f;
+  }
+
+  const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
+  const int grp = lane / kCPR;  // token group of this lane in the PV layout
+  const int col = lane % kCPR;  // 16-byte column of this lane in the PV layout
+  const int t_row = lane % kTok;
+
+  for (int c0 = start; c0 < end; c0 += kTok) {
+    const int64_t blk = table[c0 / kBlockSize];
+    const int64_t row0 = ((blk * a.num_kv_heads + g) * kBlockSize + (c0 % kBlockSize));
+    const uint8_t* kt = a.k_cache + row0 * S::kRowBytes;
+    const uint8_t* vt = a.v_cache + row0 * S::kRowBytes;
+    u32x4 kr[S::kLoads], vr[S::kLoads];
+#pragma unroll
+    for (int i = 0; i < S::kLoads; ++i)
+      kr[i] = *reinterpret_cast<const u32x4*>(kt + i * 1024 + lane * 16);
+#pragma unroll
+    for (int i = 0; i < S::kLoads; ++i)
+      vr[i] = *reinterpret_cast<const u32x4*>(vt + i * 1024 + lane * 16);
+
+    __syncthreads();  // previous chunk's LDS reads are done
+#pragma unroll
+    for (int i = 0; i < S::kLoads; ++i) {
+      const int r = i * S::kRowsPerLoad + grp;
+      k_lds[r * (kCPR + 1) + col] = kr[i];
+    }
+    __syncthreads();
+
+    const int nvalid = min(kTok, end - c0);
+
+    // scores: lane t_row owns token c0 + t_row.  q is re-read from LDS for
+    // every chunk: an opaque zero offset keeps the compiler from hoisting all
+    // of q (64 VGPRs per head) out of the loop.
+    int qz;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(qz));
+    const u32x4* qrow = q_lds + qz;
+    float sc[kHeads];
+#pragma unroll
+    for (int h = 0; h < kHeads; ++h) sc[h] = 0.f;
+#pragma unroll 2
+    for (int c = 0; c < kCPR; ++c) {
+      const u32x4 kv = k_lds[t_row * (kCPR + 1) + c];
+#pragma unroll
+      for (int h = 0; h < kHeads; ++h) {
+        const u32x4 qv = qrow[h * kCPR + c];
+        if constexpr (kElemBytes == 2) {
+          sc[h] = dot2_bf16(kv[0], qv[0], sc[h]);
+          sc[h] = dot2_bf16(kv[1], qv[1], sc[h]);
+          sc[h] = dot2_bf16(kv[2], qv[2], sc[h]);
+          sc[h] = dot2_bf16(kv[3], qv[3], sc[h]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sc[h] = fmaf(__uint_as_float(kv[e]), __uint_as_float(qv[e]), sc[h]);
+        }
+      }
+    }
+
+    const bool tok_valid = (lane < kTok) && (t_row < nvalid);
+#pragma unroll
+    for (int h = 0; h < kHeads; ++h) {
+      const float x = tok_valid ? sc[h] * a.scale_log2 : -INFINITY;
+      const float mn = fmaxf(m[h], wave_max(x));  // finite: the chunk has a valid token
+      const float alpha = fast_exp2(m[h] - mn);
+      const float p = fast_exp2(x - mn);
+      lsum[h] = lsum[h] * alpha + p;
+      m[h] = mn;
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) acc[h][e] *= alpha;
+      if (lane < kTok) p_lds[t_row * kHeads + h] = p;
+    }
+    __syncthreads();
+
+    // PV: lane holds kVec dims (column col) of tokens i*kRowsPerLoad + grp
+#pragma unroll
+    for (int i = 0; i < S::kLoads; ++i) {
+      const int r = i * S::kRowsPerLoad + grp;
+      float vals[kVec];
+      unpack<kElemBytes>(vr[i], vals);
+      if (r >= nvalid) {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) vals[e] = 0.f;
+      }
+#pragma unroll
+      for (int h = 0; h < kHeads; ++h) {
+        const float p = p_lds[r * kHeads + h];
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) acc[h][e] = fmaf(p, vals[e], acc[h][e]);
+      }
+    }
+  }
+
+  // sum the token groups (lanes col, col + kCPR, ...) and the per-lane l
+#pragma unroll
+  for (int h = 0; h < kHeads; ++h) {
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) {
+#pragma unroll
+      for (int o = kCPR; o < 64; o <<= 1) acc[h][e] += __shfl_xor(acc[h][e], o, 64);
+    }
+    lsum[h] = wave_sum(lsum[h]);
+  }
+
+  if (lane < kCPR) {
+    if (nsplit_b == 1) {
+#pragma unroll
+      for (int h = 0; h < kHeads; ++h) {
+        const float inv = 1.0f / lsum[h];
+        uint8_t* o = a.out + ((int64_t)b * a.num_q_heads + h0 + h) * S::kRowBytes + col * 16;
+        u32x4 w;
+        if constexpr (kElemBytes == 2) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w[i] = pack_bf16(acc[h][2 * i] * inv, acc[h][2 * i + 1] * inv);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(acc[h][i] * inv);
+        }
+        *reinterpret_cast<u32x4*>(o) = w;
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < kHeads; ++h) {
+        const int64_t slot = ((int64_t)b * a.num_q_heads + h0 + h) * a.nsplit + s;
+        float* dst = a.ws_acc + slot * kHeadDim + col * kVec;
+#pragma unroll
+        for (int e = 0; e < kVec; e += 4)
+          *reinterpret_cast<f32x4*>(dst + e) =
+              f32x4{acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]};
+        if (lane == 0) {
+          a.ws_ml[slot * 2] = m[h];
+          a.ws_ml[slot * 2 + 1] = lsum[h];
+        }
+      }
+    }
+  }
+}
+
+// Merge split partials of one (sequence, head) per wavefront, in split order.
+template <int kElemBytes>
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= a.batch * a.num_q_heads) return;
+  const int b = pair / a.num_q_heads;
+  const int n = a.context_lens[b];
+  const int ns = (n + a.split_tokens - 1) / a.split_tokens;
+  if (ns <= 1) return;
+  const int64_t base = (int64_t)pair * a.nsplit;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.ws_ml[(base + s) * 2]);
+  float L = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float f = fast_exp2(a.ws_ml[(base + s) * 2] - M);
+    L = fmaf(f, a.ws_ml[(base + s) * 2 + 1], L);
+    const float* src = a.ws_acc + (base + s) * kHeadDim + lane * 2;
+    o0 = fmaf(f, src[0], o0);
+    o1 = fmaf(f, src[1], o1);
+  }
+  const float inv = 1.0f / L;
+  if constexpr (kElemBytes == 2) {
+    uint32_t* o = reinterpret_cast<uint32_t*>(a.out + (int64_t)pair * kHeadDim * 2) + lane;
+    *o = pack_bf16(o0 * inv, o1 * inv);
+  } else {
+    float* o = reinterpret_cast<float*>(a.out + (int64_t)pair * kHeadDim * 4) + lane * 2;
+    o[0] = o0 * inv;
+    o[1] = o1 * inv;
+  }
+}
+
+template <int kElemBytes, int kHeads>
+void launch_split(const DecodeArgs& args, unsigned grid, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_split_kernel<kElemBytes, kHeads>), dim3(grid), dim3(64), 0, stream,
+                     args);
+}
+
+template <int kElemBytes>
+void launch_split_heads(int heads, const DecodeArgs& args, unsigned grid, hipStream_t stream) {
+  switch (heads) {
+    case 1: launch_split<kElemBytes, 1>(args, grid, stream); break;
+    case 2: launch_split<kElemBytes, 2>(args, grid, stream); break;
+    case 4: launch_split<kElemBytes, 4>(args, grid, stream); break;
+    default: launch_split<kElemBytes, 8>(args, grid, stream); break;
+  }
+}
+
+}  // namespace
+
+int decode_heads_per_wg(int group) {
+  if (group == 1 || group == 2 || group == 4 || group == 8) return group;
+  if (group > 8 && group % 8 == 0) return 8;
+  return 0;
+}
+
+bool plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_context_len,
+                 int num_splits, DecodePlan* plan) {
+  const int group = num_q_heads / num_kv_heads;
+  const int hpw = decode_heads_per_wg(group);
+  if (hpw == 0) return false;
+  plan->group = group;
+  plan->heads_per_wg = hpw;
+  plan->head_chunks = group / hpw;
+  const int64_t units = (int64_t)batch * num_kv_heads * plan->head_chunks;
+  const int max_chunks = max_context_len > 0 ? (max_context_len + 63) / 64 : 1;
+  int64_t want;
+  if (num_splits > 0) {
+    want = num_splits;
+  } else {
+    want = units > 0 ? (kTargetWaves + units - 1) / units : 1;
+  }
+  if (want < 1) want = 1;
+  if (want > max_chunks) want = max_chunks;
+  const int per = max_context_len > 0 ? (int)((max_context_len + want - 1) / want) : 64;
+  plan->split_tokens = ((per + 63) / 64) * 64;
+  plan->nsplit = max_context_len > 0 ? (max_context_len + plan->split_tokens - 1) / plan->split_tokens : 1;
+  plan->workspace_bytes =
+      plan->nsplit > 1
+          ? (size_t)batch * num_q_heads * plan->nsplit * (kHeadDim + 2) * sizeof(float)
+          : 0;
+  return true;
+}
+
+hipError_t launch_decode(int elem_bytes, const DecodePlan& plan, const DecodeLaunch& l,
+                         hipStream_t stream) {
+  DecodeArgs a;
+  a.q = (const uint8_t*)l.q;
+  a.q_stride_bytes = l.q_stride * elem_bytes;
+  a.k_cache = (const uint8_t*)l.k_cache;
+  a.v_cache = (const uint8_t*)l.v_cache;
+  a.block_tables = l.block_tables;
+  a.max_blocks = l.max_blocks;
+  a.context_lens = l.context_lens;
+  a.batch = l.batch;
+  a.num_q_heads = l.num_q_heads;
+  a.num_kv_heads = l.num_kv_heads;
+  a.group = plan.group;
+  a.head_chunks = plan.head_chunks;
+  a.scale_log2 = l.scale * kLog2e;
+  a.split_tokens = plan.split_tokens;
+  a.nsplit = plan.nsplit;
+  a.out = (uint8_t*)l.out;
+  a.ws_acc = l.workspace;
+  a.ws_ml = l.workspace
+                ? l.workspace + (size_t)l.batch * l.num_q_heads * plan.nsplit * kHeadDim
+                : nullptr;
+  const int64_t grid =
+      (int64_t)plan.nsplit * l.batch * l.num_kv_heads * plan.head_chunks;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (elem_bytes == 2)
+    launch_split_heads<2>(plan.heads_per_wg, a, (unsigned)grid, stream);
+  else
+    launch_split_heads<4>(plan.heads_per_wg, a, (unsigned)grid, stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.nsplit <= 1) return e;
+  const int64_t pairs = (int64_t)l.batch * l.num_q_heads;
+  const unsigned mgrid = (unsigned)((pairs + 3) / 4);
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL(decode_merge_kernel<2>, dim3(mgrid), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_merge_kernel<4>, dim3(mgrid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,153 @@
+"""The C ABI on the CPU: the library loads, exports every symbol the header
+declares, and rejects bad host arguments with the documented status before
+touching HIP (no kernel is launched here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_325_amd as pkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+BF16, FP32 = pkv.PKV_BF16, pkv.PKV_FP32
+OK, INVALID, UNSUPPORTED, WORKSPACE = pkv.PKV_OK, pkv.PKV_ERR_INVALID, pkv.PKV_ERR_UNSUPPORTED, pkv.PKV_ERR_WORKSPACE
+
+# a fake, 16-byte aligned, never-dereferenced device address
+FAKE = 0x10000
+
+
+def _declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = pkv.load_library()
+    syms = _declared_symbols()
+    assert set(syms) >= {"pkv_kv_store", "pkv_paged_decode", "pkv_paged_prefill_varlen",
+                         "pkv_paged_decode_workspace_bytes", "pkv_last_error"}
+    for s in syms:
+        assert hasattr(lib, s), s
+    # and nm agrees that they are exported C symbols
+    raw = ctypes.CDLL(pkv.lib_path())
+    for s in syms:
+        getattr(raw, s)
+
+
+def test_block_bytes():
+    assert pkv.pkv_kv_block_bytes(BF16, 8, 128, 256) == 256 * 8 * 128 * 2
+    assert pkv.pkv_kv_block_bytes(FP32, 8, 128, 256) == 256 * 8 * 128 * 4
+    assert pkv.pkv_kv_block_bytes(7, 8, 128, 256) == -1
+    assert pkv.pkv_kv_block_bytes(BF16, 0, 128, 256) == -1
+
+
+def _store(**kw):
+    a = dict(dtype=BF16, k=FAKE, ks=1024, v=FAKE, vs=1024, kc=FAKE, vc=FAKE, slots=FAKE, n=4,
+             hkv=8, d=128, bs=256, nblk=16)
+    a.update(kw)
+    lib = pkv.load_library()
+    return lib.pkv_kv_store(a["dtype"], a["k"], a["ks"], a["v"], a["vs"], a["kc"], a["vc"],
+                            a["slots"], a["n"], a["hkv"], a["d"], a["bs"], a["nblk"], None)
+
+
+def test_kv_store_errors():
+    assert _store(n=0) == OK  # nothing to do: no launch
+    assert _store(n=-1) == INVALID
+    assert _store(k=None) == INVALID
+    assert _store(slots=None) == INVALID
+    assert _store(dtype=5) == INVALID
+    assert _store(d=64) == UNSUPPORTED
+    assert _store(bs=16) == UNSUPPORTED
+    assert _store(hkv=0) == INVALID
+    assert _store(ks=100) == INVALID  # smaller than a row
+    assert _store(ks=1028) == INVALID  # rows not 16-byte aligned
+    assert _store(k=FAKE + 2) == INVALID
+    assert _store(nblk=0) == INVALID
+    assert "aligned" in pkv.pkv_last_error() or "num_blocks" in pkv.pkv_last_error()
+
+
+def _decode(**kw):
+    a = dict(dtype=BF16, q=FAKE, qs=16 * 128, kc=FAKE, vc=FAKE, bt=FAKE, mb=16, ctx=FAKE,
+             maxctx=4096, batch=4, hq=16, hkv=8, d=128, bs=256, nblk=64, scale=0.088,
+             splits=0, out=FAKE, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    lib = pkv.load_library()
+    return lib.pkv_paged_decode(a["dtype"], a["q"], a["qs"], a["kc"], a["vc"], a["bt"], a["mb"],
+                                a["ctx"], a["maxctx"], a["batch"], a["hq"], a["hkv"], a["d"],
+                                a["bs"], a["nblk"], a["scale"], a["splits"], a["out"], a["ws"],
+                                a["wsb"], None)
+
+
+def test_decode_errors():
+    assert _decode(batch=0) == OK
+    assert _decode(batch=-1) == INVALID
+    assert _decode(hq=12) == INVALID  # 12 % 8
+    assert _decode(hq=24) == UNSUPPORTED  # group of 3
+    assert _decode(hq=0) == INVALID
+    assert _decode(d=256) == UNSUPPORTED
+    assert _decode(bs=128) == UNSUPPORTED
+    assert _decode(maxctx=16 * 256 + 1) == INVALID  # beyond the table
+    assert _decode(q=None) == INVALID
+    assert _decode(out=FAKE + 8) == INVALID
+    assert _decode(qs=100) == INVALID
+    assert _decode(scale=float("nan")) == INVALID
+    assert _decode(splits=-2) == INVALID
+    assert _decode(ws=None, wsb=0) == WORKSPACE
+    need = pkv.pkv_paged_decode_workspace_bytes(4, 16, 8, 128, 4096, 256, 0)
+    assert need > 0
+    assert _decode(wsb=need - 4) == WORKSPACE
+
+
+def test_decode_split_plan():
+    # a multiple of 64 keys per split, consistent with the workspace size
+    for batch, hq, hkv, maxctx, splits in [(64, 16, 8, 4096, 0), (256, 32, 8, 8192, 0),
+                                           (16, 32, 8, 32768, 0), (4, 16, 8, 511, 0),
+                                           (4, 16, 8, 511, 3), (3, 8, 2, 5000, 7), (2, 4, 2, 0, 0)]:
+        S = pkv.pkv_paged_decode_split_tokens(batch, hq, hkv, 128, maxctx, 256, splits)
+        assert S > 0 and S % 64 == 0
+        ns = max(1, -(-maxctx // S))
+        ws = pkv.pkv_paged_decode_workspace_bytes(batch, hq, hkv, 128, maxctx, 256, splits)
+        assert ws == (0 if ns == 1 else batch * hq * ns * 130 * 4)
+        if splits:
+            assert ns <= splits
+    assert pkv.pkv_paged_decode_split_tokens(4, 16, 8, 128, 4096, 256, 1) >= 4096
+    assert pkv.pkv_paged_decode_workspace_bytes(4, 16, 8, 64, 4096, 256, 0) == 0  # unsupported
+
+
+def _prefill(**kw):
+    a = dict(dtype=BF16, q=FAKE, qs=32 * 128, kc=FAKE, vc=FAKE, cu=FAKE, maxq=100, ctx=FAKE,
+             maxctx=612, bt=FAKE, mb=4, batch=2, hq=32, hkv=8, d=128, bs=256, nblk=8,
+             scale=0.088, causal=1, out=FAKE)
+    a.update(kw)
+    lib = pkv.load_library()
+    return lib.pkv_paged_prefill_varlen(a["dtype"], a["q"], a["qs"], a["kc"], a["vc"], a["cu"],
+                                        a["maxq"], a["ctx"], a["maxctx"], a["bt"], a["mb"],
+                                        a["batch"], a["hq"], a["hkv"], a["d"], a["bs"], a["nblk"],
+                                        a["scale"], a["causal"], a["out"], None)
+
+
+def test_prefill_errors():
+    assert _prefill(batch=0) == OK
+    assert _prefill(maxq=0) == OK
+    assert _prefill(causal=0) == INVALID
+    assert _prefill(dtype=FP32) == UNSUPPORTED
+    assert _prefill(hq=24) == UNSUPPORTED  # group of 3
+    assert _prefill(d=64) == UNSUPPORTED
+    assert _prefill(maxctx=5 * 256) == INVALID
+    assert _prefill(cu=None) == INVALID
+    assert _prefill(q=FAKE + 4) == INVALID
+    assert _prefill(batch=-3) == INVALID
+    assert "causal" in (_prefill(causal=2) and pkv.pkv_last_error())
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 8, 128, dtype=torch.bfloat16)
+    c = torch.zeros(2, 8, 256, 128, dtype=torch.bfloat16)
+    s = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        pkv.pkv_kv_store(x, x, c, c, s)

@@ -1,0 +1,242 @@
+"""GPU parity: the HIP library against the CPU oracle on the same seeded inputs.
+
+Store: bit-exact over the whole cache.  Attention: within max-abs 2e-2 and
+mean-abs 2e-3 of the fp64 oracle (bf16 or fp32 inputs, fp32 accumulation).
+Small cases cover every row; the five full-size workloads are checked on all
+rows where the oracle is quick and on sampled sequences / rows otherwise,
+in the launch configuration the benchmark uses (automatic split plan)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_325_amd as pkv
+from oracle import ref
+from tests.gpu_helpers import (DeviceWorkload, announce, assert_close, attend, check_inputs,
+                               store, to_device)
+from tests.oracle_helpers import expected, q64, sequence_view, stored_bits
+from workloads import Spec, bits_view, build, config, small_specs
+
+pytestmark = pytest.mark.gpu
+
+SMALL = small_specs()
+SMALL_IDS = [s.name for s in SMALL]
+
+
+def _cache_bits(t: torch.Tensor) -> np.ndarray:
+    return bits_view(t.cpu())
+
+
+def _run_step(w, num_splits=0):
+    d = to_device(w)
+    check_inputs(d)
+    announce(f"{w.spec.name}: kv_store")
+    store(d)
+    announce(f"{w.spec.name}: attention (num_splits={num_splits})")
+    out = attend(d, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return d, out
+
+
+# ---------------------------------------------------------------------------
+# small cases: every row
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("spec", SMALL, ids=SMALL_IDS)
+def test_small_store_bit_exact(spec):
+    w = build(spec)
+    d, _ = _run_step(w)
+    kcb, vcb = stored_bits(w)
+    assert np.array_equal(_cache_bits(d.k_cache), kcb)
+    assert np.array_equal(_cache_bits(d.v_cache), vcb)
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=SMALL_IDS)
+def test_small_attention(spec):
+    w = build(spec)
+    _, out = _run_step(w)
+    want = expected(w)
+    assert_close(out.to(torch.float64).cpu().numpy(), want, spec.name)
+    if w.dtype == "fp32":  # fp32 inputs: much tighter than the bf16 bound
+        assert np.abs(out.to(torch.float64).cpu().numpy() - want).max() < 1e-4
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 8, 64])
+def test_decode_forced_splits(splits):
+    w = build([s for s in SMALL if s.name == "dec-bf16-g4-long"][0])
+    _, out = _run_step(w, num_splits=splits)
+    assert_close(out.to(torch.float64).cpu().numpy(), expected(w), f"splits={splits}")
+
+
+def test_split_partials_in_workspace():
+    """The split-K partials (acc, m, l) the decode kernel leaves in the
+    workspace match the oracle's partials for the same split size."""
+    w = build([s for s in SMALL if s.name == "dec-bf16-g4-long"][0])
+    d = to_device(w)
+    check_inputs(d)
+    store(d)
+    splits = 4
+    args = (w.batch, w.num_q_heads, w.num_kv_heads, 128, w.max_context_len, 256, splits)
+    S = pkv.pkv_paged_decode_split_tokens(*args)
+    nbytes = pkv.pkv_paged_decode_workspace_bytes(*args)
+    ns = -(-w.max_context_len // S)
+    assert nbytes == w.batch * w.num_q_heads * ns * 130 * 4
+    ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    announce("workspace partials: decode")
+    attend(d, num_splits=splits, workspace=ws)
+    torch.cuda.synchronize()
+    nacc = w.batch * w.num_q_heads * ns * 128
+    acc = ws[:nacc].view(w.batch, w.num_q_heads, ns, 128).cpu().double().numpy()
+    ml = ws[nacc:].view(w.batch, w.num_q_heads, ns, 2).cpu().double().numpy()
+    kcb, vcb = stored_bits(w)
+    parts = ref.decode_partials(q64(w), ref.widen(kcb, w.dtype), ref.widen(vcb, w.dtype),
+                                w.block_tables, w.context_lens, w.scale, S)
+    log2e = 1.0 / math.log(2.0)
+    checked = 0
+    for b, (pacc, pm, pl) in enumerate(parts):
+        nsb = pacc.shape[0]
+        if nsb <= 1:
+            continue  # single-split sequences write their output directly
+        for s in range(nsb):
+            for h in range(w.num_q_heads):
+                assert abs(ml[b, h, s, 0] - pm[s, h] * log2e) < 1e-3
+                assert abs(ml[b, h, s, 1] - pl[s, h]) <= 2e-3 * pl[s, h]
+                scale = max(1.0, np.abs(pacc[s, h]).max())
+                assert np.abs(acc[b, h, s] - pacc[s, h]).max() <= 2e-2 * scale
+                checked += 1
+    assert checked > 0
+
+
+# ---------------------------------------------------------------------------
+# invariants on the GPU result
+# ---------------------------------------------------------------------------
+
+def _decode_out(d, **kw):
+    out = attend(d, **kw)
+    torch.cuda.synchronize()
+    return out.clone()
+
+
+def test_decode_deterministic_and_permutation_bit_exact():
+    w = build([s for s in SMALL if s.name == "dec-bf16-g4-long"][0])
+    d = to_device(w)
+    check_inputs(d)
+    store(d)
+    announce("determinism: decode twice")
+    a = _decode_out(d)
+    b = _decode_out(d)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    # permute the physical blocks and the table: reduction order is logical,
+    # so the result must not change by a single bit
+    pi = torch.from_numpy(np.random.default_rng(5).permutation(w.num_blocks)).cuda()
+    kc2 = torch.empty_like(d.k_cache)
+    vc2 = torch.empty_like(d.v_cache)
+    kc2[pi] = d.k_cache
+    vc2[pi] = d.v_cache
+    bt = d.block_tables.long()
+    bt2 = torch.where(bt >= 0, pi[bt.clamp(min=0)], bt).int().contiguous()
+    announce("permutation: decode on permuted pool")
+    c = pkv.pkv_paged_decode(d.q, kc2, vc2, bt2, d.context_lens, w.max_context_len, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+
+
+def test_shared_prefix_equals_private_copies_bit_exact():
+    w = build([s for s in SMALL if s.name == "dec-bf16-shared"][0])
+    d = to_device(w)
+    check_inputs(d)
+    store(d)
+    announce("shared prefix: decode")
+    a = _decode_out(d)
+    bt = w.block_tables.copy()
+    extra = []
+    nxt = w.num_blocks
+    for b in range(w.batch):
+        for i in range(bt.shape[1]):
+            if bt[b, i] >= 0 and int(bt[b, i]) in w.shared_physical:
+                extra.append(int(bt[b, i]))
+                bt[b, i] = nxt
+                nxt += 1
+    idx = torch.tensor(extra, device="cuda", dtype=torch.long)
+    kc2 = torch.cat([d.k_cache, d.k_cache[idx]]).contiguous()
+    vc2 = torch.cat([d.v_cache, d.v_cache[idx]]).contiguous()
+    bt2 = torch.from_numpy(bt).cuda()
+    announce("shared prefix: decode on private copies")
+    c = pkv.pkv_paged_decode(d.q, kc2, vc2, bt2, d.context_lens, w.max_context_len, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_context_one_returns_v_row_bit_exact(dtype):
+    w = build(Spec("ctx1", "decode", dtype, 8, 2, [1, 1, 1, 1], [1] * 4, 4242))
+    d, out = _run_step(w)
+    v = d.v.contiguous()  # the stored V rows, [batch, Hkv, D]
+    for h in range(8):
+        assert torch.equal(out[:, h], v[:, h // 4]), f"head {h}"
+
+
+def test_prefill_single_query_matches_decode():
+    ctx = [1, 300, 513, 1024, 2000]
+    wp = build(Spec("p1", "prefill", "bf16", 8, 2, ctx, [1] * 5, 777))
+    dp, outp = _run_step(wp)
+    # the same inputs through decode
+    announce("decode of the same single queries")
+    outd = pkv.pkv_paged_decode(dp.q, dp.k_cache, dp.v_cache, dp.block_tables, dp.context_lens,
+                                wp.max_context_len, wp.scale)
+    torch.cuda.synchronize()
+    assert_close(outp.double().cpu().numpy(), outd.double().cpu().numpy(), "prefill vs decode")
+    assert_close(outp.double().cpu().numpy(), expected(wp), "prefill vs oracle")
+
+
+# ---------------------------------------------------------------------------
+# the five full-size workloads
+# ---------------------------------------------------------------------------
+
+def _seq_sample(w, index):
+    if index != 4:
+        return list(range(w.batch))
+    rng = np.random.default_rng(4)
+    return sorted({int(np.argmin(w.context_lens)), int(np.argmax(w.context_lens))}
+                  | set(rng.choice(w.batch, 22, replace=False).tolist()))
+
+
+def _prefill_rows(w):
+    rng = np.random.default_rng(3)
+    rows = set()
+    for b in range(w.batch):
+        lo, hi = int(w.cu_seqlens_q[b]), int(w.cu_seqlens_q[b + 1])
+        for i in (0, 1, 31, 32, 63, 64, 127, 128, hi - lo - 2, hi - lo - 1):
+            if 0 <= i < hi - lo:
+                rows.add(lo + i)
+        rows.update((lo + rng.integers(0, hi - lo, 4)).tolist())
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("index", [1, 2, 3, 4, 5])
+def test_config(index):
+    """Whole step at full size: store bit-exact over both caches, then the
+    attention output of every (decode) sequence -- a sample of 24 sequences
+    for the 256-sequence workload -- or of sampled query rows (prefill)."""
+    w = config(index)
+    d, out_t = _run_step(w)
+    out = out_t.double().cpu().numpy()
+    kcb, vcb = stored_bits(w)
+    assert np.array_equal(_cache_bits(d.k_cache), kcb), "k_cache after store"
+    assert np.array_equal(_cache_bits(d.v_cache), vcb), "v_cache after store"
+    del d
+    q = q64(w)
+    if w.spec.mode == "decode":
+        for b in _seq_sample(w, index):
+            kc, vc, row = sequence_view(w, kcb, vcb, b)
+            want = ref.decode(q[b : b + 1], kc, vc, row[None, :], w.context_lens[b : b + 1],
+                              w.scale)
+            assert_close(out[b : b + 1], want, f"config {index} sequence {b}")
+    else:
+        kc, vc = ref.widen(kcb, w.dtype), ref.widen(vcb, w.dtype)
+        rows = _prefill_rows(w)
+        want = ref.prefill(q, kc, vc, w.cu_seqlens_q, w.context_lens, w.block_tables, w.scale,
+                           rows=rows)
+        assert_close(out[rows], want[rows], f"config {index} sampled rows")
