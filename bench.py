@@ -1,0 +1,356 @@
+"""Benchmark of the paged KV-cache hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+                    [--no-extra] [--no-cpu] [--copy-calibration]
+
+One step = the whole per-layer hot path over one batch of the workload:
+``pkv_kv_store`` of this step's tokens, then ``pkv_paged_decode`` (decode
+workloads) or ``pkv_paged_prefill_varlen`` (the prefill workload), inputs
+already resident in HBM.  Before every step (warm-up and timed) a 1 GiB buffer
+is *read* (a row-wise max) to evict the 256 MB MALL, so every step reads the
+KV cache from HBM.  The eviction reads rather than writes: a write would leave
+up to 256 MB of dirty lines whose write-back would then be charged to the
+measured step.  The step itself is timed with HIP events recorded on the
+stream the kernels run on, which excludes the eviction.  The timed region (K steps) is
+bracketed by device synchronisation.
+
+The headline line is the 64-sequence bf16 decode layer (context lengths
+U[512, 4096], 16 q / 8 kv heads).  ``value`` is the step's algorithmic bytes
+(stored K/V rows read and written, the context's K and V, q and out) per
+second.  ``roofline`` covers the dominant kernel, the decode kernel: its
+algorithmic bytes per launch over its mean event-timed duration, against the
+8 TB/s HBM peak.  ``cpu_baseline`` times the CPU oracle on the same workload
+(bounded to ~10 s, one thread).  ``extra`` reports the other workloads with
+the same method (prefill against the 2.5 PFLOP/s dense bf16 MFMA peak).
+Prints exactly one JSON line on stdout.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+FLUSH_BYTES = 1 << 30
+
+METRIC = "paged decode KV GB/s (% HBM peak) + tokens/s; prefill TFLOP/s (% MFMA peak)"
+
+
+def log(msg: str) -> None:
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+class Device:
+    """Workload tensors on the GPU (the generator's CPU tensors, copied)."""
+
+    def __init__(self, w, torch):
+        import numpy as np
+
+        self.w = w
+        dev = "cuda"
+
+        def i32(a):
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+        self.qkv = w.qkv.to(dev)
+        self.k_cache = w.k_cache.to(dev)
+        self.v_cache = w.v_cache.to(dev)
+        self.slot_mapping = i32(w.slot_mapping)
+        self.block_tables = i32(w.block_tables)
+        self.context_lens = i32(w.context_lens)
+        self.cu_seqlens_q = i32(w.cu_seqlens_q)
+        hq, hkv = w.num_q_heads, w.num_kv_heads
+        self.q = self.qkv[:, :hq]
+        self.k = self.qkv[:, hq : hq + hkv]
+        self.v = self.qkv[:, hq + hkv : hq + 2 * hkv]
+        self.out = torch.empty((w.num_tokens, hq, w.head_dim), dtype=w.torch_dtype, device=dev)
+        self.workspace = None
+        if w.spec.mode == "decode":
+            import paged_kv_cache_325_amd as pkv
+
+            need = pkv.pkv_paged_decode_workspace_bytes(w.batch, hq, hkv, w.head_dim,
+                                                        w.max_context_len, w.block_size, 0)
+            if need:
+                self.workspace = torch.zeros(need // 4, dtype=torch.float32, device=dev)
+
+    def check(self):
+        """Host-side check of every index the kernels will follow."""
+        import numpy as np
+
+        w = self.w
+        B = w.block_size
+        nb = -(-w.context_lens.astype(np.int64) // B)
+        assert (nb <= w.block_tables.shape[1]).all()
+        for b in range(w.batch):
+            row = w.block_tables[b, : nb[b]]
+            assert ((row >= 0) & (row < w.num_blocks)).all()
+        s = w.slot_mapping
+        assert ((s == -1) | ((s >= 0) & (s < w.num_blocks * B))).all()
+
+    def store(self):
+        import paged_kv_cache_325_amd as pkv
+
+        pkv.pkv_kv_store(self.k, self.v, self.k_cache, self.v_cache, self.slot_mapping)
+
+    def attend(self):
+        import paged_kv_cache_325_amd as pkv
+
+        w = self.w
+        if w.spec.mode == "decode":
+            pkv.pkv_paged_decode(self.q, self.k_cache, self.v_cache, self.block_tables,
+                                 self.context_lens, w.max_context_len, w.scale, out=self.out,
+                                 workspace=self.workspace)
+        else:
+            pkv.pkv_paged_prefill_varlen(self.q, self.k_cache, self.v_cache, self.cu_seqlens_q,
+                                         w.max_seqlen_q, self.context_lens, w.max_context_len,
+                                         self.block_tables, w.scale, out=self.out)
+
+
+def make_flush(torch):
+    """A read-only MALL eviction: row-wise max over a 1 GiB buffer."""
+    buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda").view(4096, -1)
+    return lambda: torch.amax(buf, dim=1)
+
+
+def time_steps(d: Device, steps: int, warmup: int, torch):
+    """Per-step (store, attention) event times in ms, MALL evicted before each."""
+    flush = make_flush(torch)
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        flush()
+        d.store()
+        d.attend()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        flush()
+        evs[i][0].record(stream)
+        d.store()
+        evs[i][1].record(stream)
+        d.attend()
+        evs[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    store_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    del flush
+    return store_ms, attn_ms, wall
+
+
+def mean(x):
+    return sum(x) / len(x)
+
+
+def measure(index: int, steps: int, warmup: int, torch):
+    from workloads import config
+
+    t = time.perf_counter()
+    w = config(index)
+    log(f"workload {index} ({w.spec.name}) generated in {time.perf_counter() - t:.1f}s")
+    d = Device(w, torch)
+    d.check()
+    store_ms, attn_ms, wall = time_steps(d, steps, warmup, torch)
+    step_ms = [a + b for a, b in zip(store_ms, attn_ms)]
+    r = {
+        "w": w,
+        "store_ms": mean(store_ms),
+        "attn_ms": mean(attn_ms),
+        "attn_ms_median": sorted(attn_ms)[len(attn_ms) // 2],
+        "step_ms": mean(step_ms),
+        "wall_s": wall,
+    }
+    kv = w.logical_kv_bytes()
+    if w.spec.mode == "decode":
+        attn_bytes = kv + w.qo_bytes()
+        r["attn_bytes"] = attn_bytes
+        r["attn_gbs"] = attn_bytes / (r["attn_ms"] * 1e-3) / 1e9
+        r["unique_gbs"] = (w.unique_kv_bytes() + w.qo_bytes()) / (r["attn_ms"] * 1e-3) / 1e9
+    else:
+        r["flops"] = w.prefill_flops()
+        r["tflops"] = r["flops"] / (r["attn_ms"] * 1e-3) / 1e12
+        # prefill reads each unique cached K/V byte at least once
+        r["attn_bytes"] = w.unique_kv_bytes() + w.qo_bytes()
+    r["step_bytes"] = w.store_bytes() + r["attn_bytes"]
+    r["step_gbs"] = r["step_bytes"] / (r["step_ms"] * 1e-3) / 1e9
+    r["store_gbs"] = w.store_bytes() / (r["store_ms"] * 1e-3) / 1e9 if r["store_ms"] > 0 else None
+    del d
+    torch.cuda.empty_cache()
+    return r
+
+
+def cpu_baseline(index: int, budget_s: float = 10.0):
+    """The CPU oracle, as it stands, on the same workload: store, then decode
+    of every sequence (one sequence at a time), repeated until ~budget_s."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import ref
+    from workloads import bits_view, config
+
+    w = config(index)
+    kb, vb = bits_view(w.k.contiguous()), bits_view(w.v.contiguous())
+    kcb0, vcb0 = bits_view(w.k_cache), bits_view(w.v_cache)
+    q = ref.widen(bits_view(w.q.contiguous()), w.dtype)
+    passes, nbytes, t0 = 0, 0, time.perf_counter()
+    with threadpool_limits(1):
+        while True:
+            kcb, vcb = ref.kv_store(kb, vb, kcb0, vcb0, w.slot_mapping, w.block_size)
+            for b in range(w.batch):
+                n = int(w.context_lens[b])
+                ids = w.block_tables[b, : ref.num_blocks(n, w.block_size)]
+                kc, vc = ref.widen(kcb[ids], w.dtype), ref.widen(vcb[ids], w.dtype)
+                ref.decode(q[b : b + 1], kc, vc, np.arange(len(ids), dtype=np.int32)[None],
+                           w.context_lens[b : b + 1], w.scale)
+            passes += 1
+            nbytes += w.store_bytes() + w.logical_kv_bytes() + w.qo_bytes()
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(nbytes / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"whole workload (store + decode of all {w.batch} sequences, numpy fp64, "
+                  f"one BLAS thread), {passes} pass(es) in {dt:.1f}s; host has "
+                  f"{os.cpu_count()} cpus",
+        "tokens_per_s": round(passes * w.batch / dt, 2),
+    }
+
+
+def copy_calibration(torch, nbytes: int = 256 << 20, reps: int = 3) -> None:
+    """Plain device copies of a known size: a reference for HBM byte counters."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {reps} copies of {nbytes} bytes")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-extra", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run plain copies of a known size (for HBM counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the hot path is "
+              "measured on one GPU's share, see the design notes for sharding", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    import paged_kv_cache_325_amd as pkv
+
+    pkv.load_library()  # fails loudly if the HIP library is missing
+    if args.copy_calibration:
+        copy_calibration(torch)
+
+    head = measure(args.workload, args.steps, args.warmup, torch)
+    w = head["w"]
+    log(f"headline: step {head['step_ms']:.4f} ms, decode {head['attn_ms']:.4f} ms, "
+        f"store {head['store_ms']:.4f} ms")
+
+    extra = {}
+    if not args.no_extra:
+        for idx in (1, 2, 3, 4, 5):
+            if idx == args.workload:
+                continue
+            r = measure(idx, max(3, args.steps // 2), max(1, args.warmup // 2), torch)
+            e = {"step_ms": round(r["step_ms"], 4), "store_ms": round(r["store_ms"], 4),
+                 "attn_ms": round(r["attn_ms"], 4)}
+            if "tflops" in r:
+                e.update(prefill_tflops=round(r["tflops"], 1),
+                         mfma_frac=round(r["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+                         prefill_tokens_per_s=round(r["w"].num_tokens / (r["attn_ms"] * 1e-3), 1))
+            else:
+                e.update(decode_gbs=round(r["attn_gbs"], 1),
+                         hbm_frac=round(r["attn_gbs"] / HBM_PEAK_GBS, 4),
+                         decode_unique_gbs=round(r["unique_gbs"], 1),
+                         decode_tokens_per_s=round(r["w"].batch / (r["attn_ms"] * 1e-3), 1))
+            extra[r["w"].spec.name] = e
+            log(f"workload {idx}: {e}")
+
+    if w.spec.mode == "decode":
+        roof = {"bound": "hbm", "achieved": round(head["attn_gbs"], 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(head["attn_gbs"] / HBM_PEAK_GBS, 4),
+                "traffic": None, "kernel": "decode_split_kernel",
+                "bytes_per_launch": head["attn_bytes"],
+                "mean_launch_ms": round(head["attn_ms"], 5)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(head["tflops"], 2),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(head["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "prefill_kernel", "flops_per_launch": head["flops"],
+                "mean_launch_ms": round(head["attn_ms"], 5)}
+
+    cpu = None
+    if not args.no_cpu and w.spec.mode == "decode":
+        log("timing the CPU oracle")
+        cpu = cpu_baseline(args.workload)
+
+    line = {
+        "metric": METRIC,
+        "value": round(head["step_gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["step_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.spec.name,
+            "batch": w.batch,
+            "num_q_heads": w.num_q_heads,
+            "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim,
+            "block_size": w.block_size,
+            "sum_context_tokens": int(w.context_lens.sum()),
+            "stored_tokens": int((w.slot_mapping >= 0).sum()),
+            "seed": w.spec.seed,
+        },
+        "decode_gbs": round(head.get("attn_gbs", 0.0), 2),
+        "decode_tokens_per_s": round(w.batch / (head["attn_ms"] * 1e-3), 1),
+        "step_tokens_per_s": round(w.batch / (head["step_ms"] * 1e-3), 1),
+        "hbm_frac": round(head.get("attn_gbs", 0.0) / HBM_PEAK_GBS, 4),
+        "store_ms": round(head["store_ms"], 5),
+        "timing": "HIP events on the kernels' stream, mean over the timed steps; 1 GiB "
+                  "read-only MALL eviction before every step (outside the events)",
+        "wall_s_timed_region": round(head["wall_s"], 3),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

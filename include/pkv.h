@@ -58,7 +58,7 @@
  * most recent non-OK status of the calling thread.
  *
  * Results are deterministic: a pure function of the inputs and the split
- * plan; no reduction uses atomics.
+ * plan: every sum runs in a fixed order and no kernel uses atomics.
  */
 #ifndef PKV_H_
 #define PKV_H_
@@ -104,10 +104,10 @@ pkv_status pkv_kv_store(pkv_dtype dtype, const void* k, int64_t k_token_stride,
                         int64_t num_blocks, void* stream);
 
 /*
- * pkv_paged_decode_workspace_bytes -- bytes of fp32 workspace that
- * pkv_paged_decode needs for the split-K partials with the same arguments
- * (0 when the plan uses a single split).  num_splits: 0 = automatic, else the
- * number of splits of max_context_len requested.  Returns 0 for invalid or
+ * pkv_paged_decode_workspace_bytes -- bytes of workspace that
+ * pkv_paged_decode needs for the split-K partials with the same
+ * arguments (0 when the plan uses a single split).  num_splits: 0 =
+ * automatic, else the number of splits of max_context_len requested.  Returns 0 for invalid or
  * unsupported arguments (pkv_paged_decode then reports the error).
  */
 size_t pkv_paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
@@ -117,8 +117,10 @@ size_t pkv_paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
 
 /*
  * pkv_paged_decode_split_tokens -- keys per split that pkv_paged_decode uses
- * with these arguments (a multiple of 64; >= max_context_len means one
- * split).  Returns 0 for invalid or unsupported arguments.
+ * with these arguments: a multiple of 64 up to 256, a multiple of 256 above,
+ * never more than 16384 (so a requested split count is an upper bound only
+ * up to that size); >= max_context_len means one split.  Returns 0 for
+ * invalid or unsupported arguments.
  */
 int32_t pkv_paged_decode_split_tokens(int32_t batch, int32_t num_q_heads,
                                       int32_t num_kv_heads, int32_t head_dim,
@@ -146,15 +148,17 @@ int32_t pkv_paged_decode_split_tokens(int32_t batch, int32_t num_q_heads,
  *   num_splits     0 = automatic; otherwise the requested number of splits
  *   out            device, [batch][num_q_heads][head_dim], dense, dtype
  *   workspace      device, >= pkv_paged_decode_workspace_bytes(...) bytes,
- *                  16-byte aligned, may be NULL when that is 0.  Layout:
- *                  float acc[batch][num_q_heads][nsplit][head_dim] followed
- *                  by float ml[batch][num_q_heads][nsplit][2], nsplit =
- *                  ceil(max_context_len / S).  For split s of sequence b
- *                  (keys s*S .. min(n,(s+1)*S)-1) with x_j = scale*q.k_j and
- *                  splits that exist (s*S < n): ml = (m, l) where m =
- *                  max_j x_j * log2(e) and l = sum_j 2^(x_j*log2(e) - m), and
- *                  acc = sum_j 2^(x_j*log2(e) - m) v_j.  Sequences with a
- *                  single split do not use their slots.
+ *                  16-byte aligned, may be NULL when that is 0; needs no
+ *                  initialisation.  Calls sharing a workspace must not
+ *                  overlap.  Layout: float acc[batch][num_q_heads][nsplit]
+ *                  [head_dim], then float ml[batch][num_q_heads][nsplit][2],
+ *                  nsplit = ceil(max_context_len / S).  For split s of a
+ *                  sequence b with more than one split (keys s*S ..
+ *                  min(n,(s+1)*S)-1, s*S < n), with x_j = scale*q.k_j:
+ *                  ml = (m, l), m = max_j x_j*log2(e), l = sum_j
+ *                  2^(x_j*log2(e) - m), and acc = sum_j 2^(x_j*log2(e) - m) v_j.
+ *                  A second kernel merges them in split order: M = max_s m_s,
+ *                  out = sum_s 2^(m_s-M) acc_s / sum_s 2^(m_s-M) l_s.
  */
 pkv_status pkv_paged_decode(pkv_dtype dtype, const void* q,
                             int64_t q_token_stride, const void* k_cache,

@@ -180,8 +180,8 @@ def pkv_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
     """Paged decode: q [batch, Hq, D] (token stride free) -> out [batch, Hq, D].
 
     ``max_context_len`` is a host integer >= every context length (it sets the
-    split plan without a device-to-host read).  ``workspace`` is allocated with
-    torch if not given."""
+    split plan without a device-to-host read).  ``workspace`` is allocated
+    with torch if not given."""
     lib = load_library()
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _gpu(t, n)

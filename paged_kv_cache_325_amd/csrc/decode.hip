@@ -32,9 +32,13 @@
 // allocation) but their score is replaced by -inf and their V by 0, so NaN
 // poison there cannot leak.
 //
-// Each split writes unnormalised (acc, m, l) to the workspace; the merge
-// kernel combines them in split order (deterministic).  A sequence with one
-// split writes its output directly.  HBM-bound: the algorithmic traffic is
+// Each split writes unnormalised (acc, m, l) to the workspace; a second,
+// small kernel merges them in split order (deterministic).  A sequence with
+// a single split writes its output directly.  The kernel boundary is what
+// makes the partials of every XCD visible to the merge: merging inside the
+// split kernel would need an agent-scope release/acquire (a full L2
+// write-back and invalidate) in every split, which costs far more than the
+// second launch.  HBM-bound: the algorithmic traffic is
 // the context's K and V bytes plus q and out.
 #include <math.h>
 
@@ -46,6 +50,7 @@ namespace pkv {
 namespace {
 
 constexpr int kTargetWaves = 256 * 32;  // 256 CUs; enough waves for balance
+constexpr int kMaxSplitTokens = 64 * kBlockSize;
 
 template <int kElemBytes>
 struct DecodeShape {
@@ -72,6 +77,9 @@ struct DecodeArgs {
   float* ws_acc;
   float* ws_ml;
 };
+
+struct TrueTag { static constexpr bool value = true; };
+struct FalseTag { static constexpr bool value = false; };
 
 template <int kElemBytes>
 __device__ __forceinline__ void unpack(const u32x4& w, float* f) {
@@ -145,26 +153,50 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const int col = lane % kCPR;  // 16-byte column of this lane in the PV layout
   const int t_row = lane % kTok;
 
-  for (int c0 = start; c0 < end; c0 += kTok) {
-    const int64_t blk = table[c0 / kBlockSize];
-    const int64_t row0 = ((blk * a.num_kv_heads + g) * kBlockSize + (c0 % kBlockSize));
-    const uint8_t* kt = a.k_cache + row0 * S::kRowBytes;
-    const uint8_t* vt = a.v_cache + row0 * S::kRowBytes;
-    u32x4 kr[S::kLoads], vr[S::kLoads];
-#pragma unroll
-    for (int i = 0; i < S::kLoads; ++i)
-      kr[i] = *reinterpret_cast<const u32x4*>(kt + i * 1024 + lane * 16);
-#pragma unroll
-    for (int i = 0; i < S::kLoads; ++i)
-      vr[i] = *reinterpret_cast<const u32x4*>(vt + i * 1024 + lane * 16);
+  // Block-table entries of this split, one per lane, loaded once: a split
+  // spans at most 64 blocks (the plan keeps split_tokens <= 64 * 256 and a
+  // multiple of 256 above 256), so the per-chunk lookup is a readlane and
+  // never a load + wait inside the pipelined loop.
+  const int tab_base = start / kBlockSize;
+  const int tab_idx = tab_base + lane;
+  const int tab = tab_idx < (end + kBlockSize - 1) / kBlockSize ? table[tab_idx] : 0;
+  // Byte offset of the (block, kv head g) rows starting at key c0.
+  auto chunk_base = [&](int c0) -> int64_t {
+    const int64_t blk = __builtin_amdgcn_readlane(tab, c0 / kBlockSize - tab_base);
+    return ((blk * a.num_kv_heads + g) * kBlockSize + (c0 % kBlockSize)) * S::kRowBytes;
+  };
 
-    __syncthreads();  // previous chunk's LDS reads are done
+  // Software pipeline: the next chunk's K is loaded as soon as the current
+  // K has been copied to LDS (reusing its registers), the next chunk's V as
+  // soon as the current V has been consumed, so both loads overlap a whole
+  // chunk of compute.  The last chunk is peeled so the loop body issues its
+  // prefetches unconditionally (a conditional load would make the compiler
+  // wait for every outstanding load at the join).
+  u32x4 kr[S::kLoads], vr[S::kLoads];
+  {
+    const int64_t base = chunk_base(start);
+#pragma unroll
+    for (int i = 0; i < S::kLoads; ++i)
+      kr[i] = stream_load(a.k_cache + base + i * 1024 + lane * 16);
+#pragma unroll
+    for (int i = 0; i < S::kLoads; ++i)
+      vr[i] = stream_load(a.v_cache + base + i * 1024 + lane * 16);
+  }
+
+  auto chunk = [&](int c0, auto prefetch_tag, int64_t next_base) {
+    constexpr bool kPrefetch = decltype(prefetch_tag)::value;
+    __syncthreads();  // one wavefront: orders the previous chunk's LDS reads
 #pragma unroll
     for (int i = 0; i < S::kLoads; ++i) {
       const int r = i * S::kRowsPerLoad + grp;
       k_lds[r * (kCPR + 1) + col] = kr[i];
     }
     __syncthreads();
+    if constexpr (kPrefetch) {
+#pragma unroll
+      for (int i = 0; i < S::kLoads; ++i)
+        kr[i] = stream_load(a.k_cache + next_base + i * 1024 + lane * 16);
+    }
 
     const int nvalid = min(kTok, end - c0);
 
@@ -197,12 +229,17 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     }
 
     const bool tok_valid = (lane < kTok) && (t_row < nvalid);
+    float x[kHeads], cmax[kHeads];
 #pragma unroll
     for (int h = 0; h < kHeads; ++h) {
-      const float x = tok_valid ? sc[h] * a.scale_log2 : -INFINITY;
-      const float mn = fmaxf(m[h], wave_max(x));  // finite: the chunk has a valid token
+      x[h] = tok_valid ? sc[h] * a.scale_log2 : -INFINITY;
+      cmax[h] = wave_max(x[h]);
+    }
+#pragma unroll
+    for (int h = 0; h < kHeads; ++h) {
+      const float mn = fmaxf(m[h], cmax[h]);  // finite: the chunk has a valid token
       const float alpha = fast_exp2(m[h] - mn);
-      const float p = fast_exp2(x - mn);
+      const float p = fast_exp2(x[h] - mn);
       lsum[h] = lsum[h] * alpha + p;
       m[h] = mn;
 #pragma unroll
@@ -228,7 +265,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         for (int e = 0; e < kVec; ++e) acc[h][e] = fmaf(p, vals[e], acc[h][e]);
       }
     }
-  }
+    if constexpr (kPrefetch) {
+#pragma unroll
+      for (int i = 0; i < S::kLoads; ++i)
+        vr[i] = stream_load(a.v_cache + next_base + i * 1024 + lane * 16);
+    }
+  };
+
+  int c0 = start;
+  for (; c0 + kTok < end; c0 += kTok) chunk(c0, TrueTag{}, chunk_base(c0 + kTok));
+  chunk(c0, FalseTag{}, 0);
 
   // sum the token groups (lanes col, col + kCPR, ...) and the per-lane l
 #pragma unroll
@@ -241,8 +287,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     lsum[h] = wave_sum(lsum[h]);
   }
 
-  if (lane < kCPR) {
-    if (nsplit_b == 1) {
+  if (nsplit_b == 1) {
+    if (lane < kCPR) {
 #pragma unroll
       for (int h = 0; h < kHeads; ++h) {
         const float inv = 1.0f / lsum[h];
@@ -257,25 +303,28 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         }
         *reinterpret_cast<u32x4*>(o) = w;
       }
-    } else {
+    }
+    return;
+  }
+
+  // ---- split-K: leave this split's partials for the merge kernel ----------
+  if (lane < kCPR) {
 #pragma unroll
-      for (int h = 0; h < kHeads; ++h) {
-        const int64_t slot = ((int64_t)b * a.num_q_heads + h0 + h) * a.nsplit + s;
-        float* dst = a.ws_acc + slot * kHeadDim + col * kVec;
+    for (int h = 0; h < kHeads; ++h) {
+      const int64_t slot = ((int64_t)b * a.num_q_heads + h0 + h) * a.nsplit + s;
+      float* dst = a.ws_acc + slot * kHeadDim + col * kVec;
 #pragma unroll
-        for (int e = 0; e < kVec; e += 4)
-          *reinterpret_cast<f32x4*>(dst + e) =
-              f32x4{acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]};
-        if (lane == 0) {
-          a.ws_ml[slot * 2] = m[h];
-          a.ws_ml[slot * 2 + 1] = lsum[h];
-        }
-      }
+      for (int e = 0; e < kVec; e += 4)
+        *reinterpret_cast<f32x4*>(dst + e) =
+            f32x4{acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]};
+      if (lane == 0) *reinterpret_cast<f32x2*>(a.ws_ml + slot * 2) = f32x2{m[h], lsum[h]};
     }
   }
 }
 
-// Merge split partials of one (sequence, head) per wavefront, in split order.
+// Merge the split partials of one (sequence, query head) per wavefront, in
+// split order: M = max_s m_s, out = sum_s 2^(m_s-M) acc_s / sum_s 2^(m_s-M) l_s.
+// Sequences with a single split were finished by the split kernel.
 template <int kElemBytes>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
@@ -287,23 +336,24 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   if (ns <= 1) return;
   const int64_t base = (int64_t)pair * a.nsplit;
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.ws_ml[(base + s) * 2]);
+  for (int t = 0; t < ns; ++t) M = fmaxf(M, a.ws_ml[(base + t) * 2]);
   float L = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float f = fast_exp2(a.ws_ml[(base + s) * 2] - M);
-    L = fmaf(f, a.ws_ml[(base + s) * 2 + 1], L);
-    const float* src = a.ws_acc + (base + s) * kHeadDim + lane * 2;
-    o0 = fmaf(f, src[0], o0);
-    o1 = fmaf(f, src[1], o1);
+  for (int t = 0; t < ns; ++t) {
+    const f32x2 ml = *reinterpret_cast<const f32x2*>(a.ws_ml + (base + t) * 2);
+    const float f = fast_exp2(ml[0] - M);
+    L = fmaf(f, ml[1], L);
+    const f32x2 v = *reinterpret_cast<const f32x2*>(a.ws_acc + (base + t) * kHeadDim + lane * 2);
+    o0 = fmaf(f, v[0], o0);
+    o1 = fmaf(f, v[1], o1);
   }
   const float inv = 1.0f / L;
+  constexpr int kRowBytes = kHeadDim * kElemBytes;
   if constexpr (kElemBytes == 2) {
-    uint32_t* o = reinterpret_cast<uint32_t*>(a.out + (int64_t)pair * kHeadDim * 2) + lane;
-    *o = pack_bf16(o0 * inv, o1 * inv);
+    reinterpret_cast<uint32_t*>(a.out + (int64_t)pair * kRowBytes)[lane] =
+        pack_bf16(o0 * inv, o1 * inv);
   } else {
-    float* o = reinterpret_cast<float*>(a.out + (int64_t)pair * kHeadDim * 4) + lane * 2;
-    o[0] = o0 * inv;
-    o[1] = o1 * inv;
+    *reinterpret_cast<f32x2*>(a.out + (int64_t)pair * kRowBytes + lane * 8) =
+        f32x2{o0 * inv, o1 * inv};
   }
 }
 
@@ -350,12 +400,18 @@ bool plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_context_l
   if (want < 1) want = 1;
   if (want > max_chunks) want = max_chunks;
   const int per = max_context_len > 0 ? (int)((max_context_len + want - 1) / want) : 64;
-  plan->split_tokens = ((per + 63) / 64) * 64;
+  // Splits of up to 256 keys are multiples of 64 (a 64-key chunk never
+  // crosses a block); longer splits are whole blocks, at most 64 of them, so
+  // the split kernel can hold a split's block-table entries in one register.
+  int split = per <= kBlockSize ? ((per + 63) / 64) * 64 : ((per + kBlockSize - 1) / kBlockSize) * kBlockSize;
+  if (split > kMaxSplitTokens) split = kMaxSplitTokens;
+  plan->split_tokens = split;
   plan->nsplit = max_context_len > 0 ? (max_context_len + plan->split_tokens - 1) / plan->split_tokens : 1;
-  plan->workspace_bytes =
-      plan->nsplit > 1
-          ? (size_t)batch * num_q_heads * plan->nsplit * (kHeadDim + 2) * sizeof(float)
-          : 0;
+  if (plan->nsplit > 1) {
+    plan->workspace_bytes = (size_t)batch * num_q_heads * plan->nsplit * (kHeadDim + 2) * 4;
+  } else {
+    plan->workspace_bytes = 0;
+  }
   return true;
 }
 
@@ -382,6 +438,7 @@ hipError_t launch_decode(int elem_bytes, const DecodePlan& plan, const DecodeLau
   a.ws_ml = l.workspace
                 ? l.workspace + (size_t)l.batch * l.num_q_heads * plan.nsplit * kHeadDim
                 : nullptr;
+
   const int64_t grid =
       (int64_t)plan.nsplit * l.batch * l.num_kv_heads * plan.head_chunks;
   if (grid <= 0) return hipSuccess;

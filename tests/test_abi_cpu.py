@@ -108,13 +108,15 @@ def test_decode_split_plan():
                                            (16, 32, 8, 32768, 0), (4, 16, 8, 511, 0),
                                            (4, 16, 8, 511, 3), (3, 8, 2, 5000, 7), (2, 4, 2, 0, 0)]:
         S = pkv.pkv_paged_decode_split_tokens(batch, hq, hkv, 128, maxctx, 256, splits)
-        assert S > 0 and S % 64 == 0
+        assert S > 0 and S % 64 == 0 and S <= 16384
+        assert S <= 256 or S % 256 == 0
         ns = max(1, -(-maxctx // S))
         ws = pkv.pkv_paged_decode_workspace_bytes(batch, hq, hkv, 128, maxctx, 256, splits)
         assert ws == (0 if ns == 1 else batch * hq * ns * 130 * 4)
-        if splits:
+        if splits and maxctx <= 16384:
             assert ns <= splits
     assert pkv.pkv_paged_decode_split_tokens(4, 16, 8, 128, 4096, 256, 1) >= 4096
+    assert pkv.pkv_paged_decode_split_tokens(4, 16, 8, 128, 32768, 256, 1) == 16384
     assert pkv.pkv_paged_decode_workspace_bytes(4, 16, 8, 64, 4096, 256, 0) == 0  # unsupported
 
 
