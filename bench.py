@@ -102,18 +102,35 @@ class Device:
 
         pkv.pkv_kv_store(self.k, self.v, self.k_cache, self.v_cache, self.slot_mapping)
 
-    def attend(self):
+    def attend_parts(self):
+        """The attention call as its kernel launches, in order: decode is the
+        split-K partials kernel then the merge kernel; prefill is one kernel."""
         import paged_kv_cache_325_amd as pkv
 
         w = self.w
         if w.spec.mode == "decode":
-            pkv.pkv_paged_decode(self.q, self.k_cache, self.v_cache, self.block_tables,
-                                 self.context_lens, w.max_context_len, w.scale, out=self.out,
-                                 workspace=self.workspace)
-        else:
+            def partials():
+                pkv.pkv_paged_decode_partials(self.q, self.k_cache, self.v_cache,
+                                              self.block_tables, self.context_lens,
+                                              w.max_context_len, w.scale, out=self.out,
+                                              workspace=self.workspace)
+
+            def merge():
+                pkv.pkv_paged_decode_merge(self.context_lens, w.max_context_len, w.num_q_heads,
+                                           w.num_kv_heads, self.out, self.workspace)
+
+            return [partials, merge]
+
+        def prefill():
             pkv.pkv_paged_prefill_varlen(self.q, self.k_cache, self.v_cache, self.cu_seqlens_q,
                                          w.max_seqlen_q, self.context_lens, w.max_context_len,
                                          self.block_tables, w.scale, out=self.out)
+
+        return [prefill]
+
+    def attend(self):
+        for part in self.attend_parts():
+            part()
 
 
 def make_flush(torch):
@@ -123,33 +140,58 @@ def make_flush(torch):
 
 
 def time_steps(d: Device, steps: int, warmup: int, torch):
-    """Per-step (store, attention) event times in ms, MALL evicted before each."""
+    """Per-step event times in ms, MALL evicted before each step: the store,
+    then each attention launch (decode: partials, merge; prefill: one)."""
     flush = make_flush(torch)
     stream = torch.cuda.current_stream()
+    parts = d.attend_parts()
     for i in range(warmup):
         flush()
         d.store()
-        d.attend()
+        for p in parts:
+            p()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 + len(parts))]
+           for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         flush()
         evs[i][0].record(stream)
         d.store()
         evs[i][1].record(stream)
-        d.attend()
-        evs[i][2].record(stream)
+        for j, p in enumerate(parts):
+            p()
+            evs[i][2 + j].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     store_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    part_ms = [[e[1 + j].elapsed_time(e[2 + j]) for e in evs] for j in range(len(parts))]
     del flush
-    return store_ms, attn_ms, wall
+    return store_ms, part_ms, wall
 
 
 def mean(x):
     return sum(x) / len(x)
+
+
+# HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE runs (KiB per
+# dispatch, scaled by the same counters on a plain 256 MiB device copy), with
+# the sha256 of the kernel source they were taken on: once the source
+# changes, the figure no longer describes the kernel and is reported as null.
+TRAFFIC = {}
+
+
+def traffic_for(kernel: str, workload: str):
+    import hashlib
+
+    rec = TRAFFIC.get((kernel, workload))
+    if rec is None:
+        return None
+    src = os.path.join(ROOT, "paged_kv_cache_325_amd", "csrc", rec["source"])
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec["sha256"]:
+            return None
+    return rec["bytes"]
 
 
 def measure(index: int, steps: int, warmup: int, torch):
@@ -160,13 +202,14 @@ def measure(index: int, steps: int, warmup: int, torch):
     log(f"workload {index} ({w.spec.name}) generated in {time.perf_counter() - t:.1f}s")
     d = Device(w, torch)
     d.check()
-    store_ms, attn_ms, wall = time_steps(d, steps, warmup, torch)
+    store_ms, part_ms, wall = time_steps(d, steps, warmup, torch)
+    attn_ms = [sum(x) for x in zip(*part_ms)]
     step_ms = [a + b for a, b in zip(store_ms, attn_ms)]
     r = {
         "w": w,
         "store_ms": mean(store_ms),
         "attn_ms": mean(attn_ms),
-        "attn_ms_median": sorted(attn_ms)[len(attn_ms) // 2],
+        "part_ms": [mean(p) for p in part_ms],
         "step_ms": mean(step_ms),
         "wall_s": wall,
     }
@@ -176,6 +219,9 @@ def measure(index: int, steps: int, warmup: int, torch):
         r["attn_bytes"] = attn_bytes
         r["attn_gbs"] = attn_bytes / (r["attn_ms"] * 1e-3) / 1e9
         r["unique_gbs"] = (w.unique_kv_bytes() + w.qo_bytes()) / (r["attn_ms"] * 1e-3) / 1e9
+        # the partials kernel reads every context K/V row and q
+        r["split_bytes"] = kv + w.qo_bytes() // 2
+        r["split_gbs"] = r["split_bytes"] / (r["part_ms"][0] * 1e-3) / 1e9
     else:
         r["flops"] = w.prefill_flops()
         r["tflops"] = r["flops"] / (r["attn_ms"] * 1e-3) / 1e12
@@ -295,11 +341,13 @@ def main() -> int:
             log(f"workload {idx}: {e}")
 
     if w.spec.mode == "decode":
-        roof = {"bound": "hbm", "achieved": round(head["attn_gbs"], 2), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(head["attn_gbs"] / HBM_PEAK_GBS, 4),
-                "traffic": None, "kernel": "decode_split_kernel",
-                "bytes_per_launch": head["attn_bytes"],
-                "mean_launch_ms": round(head["attn_ms"], 5)}
+        roof = {"bound": "hbm", "achieved": round(head["split_gbs"], 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(head["split_gbs"] / HBM_PEAK_GBS, 4),
+                "traffic": traffic_for("decode_split_kernel", w.spec.name),
+                "kernel": "decode_split_kernel (pkv_paged_decode_partials)",
+                "bytes_per_launch": head["split_bytes"],
+                "mean_launch_ms": round(head["part_ms"][0], 5),
+                "merge_kernel_mean_ms": round(head["part_ms"][1], 5)}
     else:
         roof = {"bound": "mfma", "achieved": round(head["tflops"], 2),
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -157,8 +157,9 @@ int32_t pkv_paged_decode_split_tokens(int32_t batch, int32_t num_q_heads,
  *                  min(n,(s+1)*S)-1, s*S < n), with x_j = scale*q.k_j:
  *                  ml = (m, l), m = max_j x_j*log2(e), l = sum_j
  *                  2^(x_j*log2(e) - m), and acc = sum_j 2^(x_j*log2(e) - m) v_j.
- *                  A second kernel merges them in split order: M = max_s m_s,
- *                  out = sum_s 2^(m_s-M) acc_s / sum_s 2^(m_s-M) l_s.
+ *                  A second kernel merges them (acc summed in split order):
+ *                  M = max_s m_s, out = sum_s 2^(m_s-M) acc_s /
+ *                  sum_s 2^(m_s-M) l_s.  pkv_paged_decode = partials + merge.
  */
 pkv_status pkv_paged_decode(pkv_dtype dtype, const void* q,
                             int64_t q_token_stride, const void* k_cache,
@@ -171,6 +172,35 @@ pkv_status pkv_paged_decode(pkv_dtype dtype, const void* q,
                             int64_t num_blocks, float scale, int32_t num_splits,
                             void* out, void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/*
+ * pkv_paged_decode_partials -- the first half of pkv_paged_decode (same
+ * arguments, same checks): for every split of every sequence it leaves the
+ * split-K partials (acc, m, l) in the workspace, and writes the output rows
+ * of sequences that have a single split.  Exposed so each half can be timed
+ * and checked on its own.
+ *
+ * pkv_paged_decode_merge -- the second half: writes the output rows of every
+ * sequence with more than one split from the partials in `workspace`
+ * (layout above), in split order.  Arguments mean what they mean for
+ * pkv_paged_decode and must equal those of the partials call (they fix the
+ * split plan).  Launches nothing when the plan has a single split.
+ */
+pkv_status pkv_paged_decode_partials(
+    pkv_dtype dtype, const void* q, int64_t q_token_stride, const void* k_cache,
+    const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, int32_t max_context_len, int32_t batch,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int64_t num_blocks, float scale, int32_t num_splits,
+    void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+pkv_status pkv_paged_decode_merge(pkv_dtype dtype, const int32_t* context_lens,
+                                  int32_t max_context_len, int32_t batch,
+                                  int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size,
+                                  int32_t num_splits, void* out,
+                                  const void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /*
  * pkv_paged_prefill_varlen -- varlen causal prefill whose keys come from the

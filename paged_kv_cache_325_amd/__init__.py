@@ -6,7 +6,8 @@ current HIP stream to the C ABI declared in ``include/pkv.h``.  All work runs
 in the library's HIP kernels; there is no CPU fallback.  If ``libpkv.so`` is
 missing or a tensor is not on the GPU, the call raises.
 
-Names follow the C ABI: ``pkv_kv_store``, ``pkv_paged_decode``,
+Names follow the C ABI: ``pkv_kv_store``, ``pkv_paged_decode`` (and its two
+halves ``pkv_paged_decode_partials`` / ``pkv_paged_decode_merge``),
 ``pkv_paged_decode_workspace_bytes``, ``pkv_paged_decode_split_tokens``,
 ``pkv_paged_prefill_varlen``, ``pkv_kv_block_bytes``, ``pkv_last_error``.
 """
@@ -22,7 +23,8 @@ import torch
 __all__ = [
     "PKV_OK", "PKV_ERR_INVALID", "PKV_ERR_UNSUPPORTED", "PKV_ERR_WORKSPACE", "PKV_ERR_HIP",
     "PKV_FP32", "PKV_BF16", "PkvError", "lib_path", "load_library",
-    "pkv_kv_store", "pkv_paged_decode", "pkv_paged_decode_workspace_bytes",
+    "pkv_kv_store", "pkv_paged_decode", "pkv_paged_decode_partials", "pkv_paged_decode_merge",
+    "pkv_paged_decode_workspace_bytes",
     "pkv_paged_decode_split_tokens", "pkv_paged_prefill_varlen", "pkv_kv_block_bytes",
     "pkv_last_error",
 ]
@@ -62,10 +64,13 @@ def load_library() -> ctypes.CDLL:
     lib.pkv_paged_decode_workspace_bytes.argtypes = [c_i32] * 7
     lib.pkv_paged_decode_split_tokens.restype = c_i32
     lib.pkv_paged_decode_split_tokens.argtypes = [c_i32] * 7
-    lib.pkv_paged_decode.restype = c_i32
-    lib.pkv_paged_decode.argtypes = [c_i32, c_p, c_i64, c_p, c_p, c_p, c_i32, c_p, c_i32, c_i32,
-                                     c_i32, c_i32, c_i32, c_i32, c_i64, c_f, c_i32, c_p, c_p,
-                                     ctypes.c_size_t, c_p]
+    for fn in (lib.pkv_paged_decode, lib.pkv_paged_decode_partials):
+        fn.restype = c_i32
+        fn.argtypes = [c_i32, c_p, c_i64, c_p, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_i32,
+                       c_i32, c_i32, c_i64, c_f, c_i32, c_p, c_p, ctypes.c_size_t, c_p]
+    lib.pkv_paged_decode_merge.restype = c_i32
+    lib.pkv_paged_decode_merge.argtypes = [c_i32, c_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                           c_i32, c_p, c_p, ctypes.c_size_t, c_p]
     lib.pkv_paged_prefill_varlen.restype = c_i32
     lib.pkv_paged_prefill_varlen.argtypes = [c_i32, c_p, c_i64, c_p, c_p, c_p, c_i32, c_p, c_i32,
                                              c_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
@@ -172,16 +177,8 @@ def pkv_paged_decode_split_tokens(batch: int, num_q_heads: int, num_kv_heads: in
         batch, num_q_heads, num_kv_heads, head_dim, max_context_len, block_size, num_splits))
 
 
-def pkv_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-                     block_tables: torch.Tensor, context_lens: torch.Tensor,
-                     max_context_len: int, scale: float, out: Optional[torch.Tensor] = None,
-                     workspace: Optional[torch.Tensor] = None, num_splits: int = 0,
-                     stream=None) -> torch.Tensor:
-    """Paged decode: q [batch, Hq, D] (token stride free) -> out [batch, Hq, D].
-
-    ``max_context_len`` is a host integer >= every context length (it sets the
-    split plan without a device-to-host read).  ``workspace`` is allocated
-    with torch if not given."""
+def _decode_call(fn_name, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
+                 scale, out, workspace, num_splits, stream):
     lib = load_library()
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _gpu(t, n)
@@ -206,11 +203,54 @@ def pkv_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
     if workspace is None and need > 0:
         workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.pkv_paged_decode(_dtype_code(q), _ptr(q), qs, _ptr(k_cache), _ptr(v_cache),
-                                _ptr(block_tables), max_blocks, _ptr(context_lens),
-                                int(max_context_len), batch, hq, hkv, d, bs, nblk, float(scale),
-                                int(num_splits), _ptr(out), _ptr(workspace), ws_bytes,
-                                _stream(stream)))
+    _check(getattr(lib, fn_name)(
+        _dtype_code(q), _ptr(q), qs, _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), max_blocks,
+        _ptr(context_lens), int(max_context_len), batch, hq, hkv, d, bs, nblk, float(scale),
+        int(num_splits), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out, workspace
+
+
+def pkv_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                     block_tables: torch.Tensor, context_lens: torch.Tensor,
+                     max_context_len: int, scale: float, out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, num_splits: int = 0,
+                     stream=None) -> torch.Tensor:
+    """Paged decode: q [batch, Hq, D] (token stride free) -> out [batch, Hq, D].
+
+    ``max_context_len`` is a host integer >= every context length (it sets the
+    split plan without a device-to-host read).  ``workspace`` is allocated
+    with torch if not given."""
+    return _decode_call("pkv_paged_decode", q, k_cache, v_cache, block_tables, context_lens,
+                        max_context_len, scale, out, workspace, num_splits, stream)[0]
+
+
+def pkv_paged_decode_partials(q, k_cache, v_cache, block_tables, context_lens, max_context_len,
+                              scale, out=None, workspace=None, num_splits=0, stream=None):
+    """First half of pkv_paged_decode: returns (out, workspace); out holds the
+    rows of single-split sequences, workspace the split-K partials."""
+    return _decode_call("pkv_paged_decode_partials", q, k_cache, v_cache, block_tables,
+                        context_lens, max_context_len, scale, out, workspace, num_splits, stream)
+
+
+def pkv_paged_decode_merge(context_lens: torch.Tensor, max_context_len: int, num_q_heads: int,
+                           num_kv_heads: int, out: torch.Tensor, workspace: Optional[torch.Tensor],
+                           num_splits: int = 0, stream=None) -> torch.Tensor:
+    """Second half of pkv_paged_decode: merge the partials in ``workspace``
+    into the rows of ``out`` [batch, Hq, D] whose sequences were split."""
+    lib = load_library()
+    _int32(context_lens, "context_lens")
+    _gpu(out, "out")
+    batch = int(context_lens.numel())
+    if out.dim() != 3 or out.shape[0] != batch or out.shape[1] != num_q_heads or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [batch, num_q_heads, head_dim] tensor")
+    d = int(out.shape[2])
+    if workspace is not None:
+        _gpu(workspace, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.pkv_paged_decode_merge(_dtype_code(out), _ptr(context_lens), int(max_context_len),
+                                      batch, int(num_q_heads), int(num_kv_heads), d, 256,
+                                      int(num_splits), _ptr(out), _ptr(workspace), ws_bytes,
+                                      _stream(stream)))
     return out
 
 

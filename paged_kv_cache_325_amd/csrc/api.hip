@@ -132,48 +132,78 @@ int32_t pkv_paged_decode_split_tokens(int32_t batch, int32_t num_q_heads, int32_
   return plan.split_tokens;
 }
 
-pkv_status pkv_paged_decode(pkv_dtype dtype, const void* q, int64_t q_token_stride,
-                            const void* k_cache, const void* v_cache,
-                            const int32_t* block_tables, int32_t max_blocks_per_seq,
-                            const int32_t* context_lens, int32_t max_context_len, int32_t batch,
-                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                            int32_t block_size, int64_t num_blocks, float scale,
-                            int32_t num_splits, void* out, void* workspace,
-                            size_t workspace_bytes, void* stream) {
-  const int eb = elem_bytes(dtype);
-  if (eb == 0) return fail(PKV_ERR_INVALID, "unknown dtype %d", (int)dtype);
+}  // extern "C"
+
+namespace {
+
+enum DecodeParts { kSplitOnly = 1, kMergeOnly = 2, kSplitAndMerge = 3 };
+
+// Checks for the merge (and shared by the split) entry points.
+pkv_status check_decode_common(pkv_dtype dtype, int32_t batch, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t max_context_len, int32_t num_splits,
+                               const int32_t* context_lens, const void* out,
+                               const void* workspace, size_t workspace_bytes,
+                               pkv::DecodePlan* plan) {
+  if (elem_bytes(dtype) == 0) return fail(PKV_ERR_INVALID, "unknown dtype %d", (int)dtype);
   if (batch < 0) return fail(PKV_ERR_INVALID, "batch (%d) < 0", batch);
-  if (max_context_len < 0 || max_blocks_per_seq < 0 || num_blocks < 0 || num_splits < 0)
-    return fail(PKV_ERR_INVALID,
-                "max_context_len, max_blocks_per_seq, num_blocks and num_splits must be >= 0");
+  if (max_context_len < 0 || num_splits < 0)
+    return fail(PKV_ERR_INVALID, "max_context_len and num_splits must be >= 0");
   pkv_status st = check_geometry(num_q_heads, num_kv_heads, head_dim, block_size);
   if (st != PKV_OK) return st;
   if (pkv::decode_heads_per_wg(num_q_heads / num_kv_heads) == 0)
     return fail(PKV_ERR_UNSUPPORTED, "GQA group size %d is not supported",
                 num_q_heads / num_kv_heads);
-  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
-    return fail(PKV_ERR_INVALID, "max_context_len (%d) > max_blocks_per_seq (%d) * block_size",
-                max_context_len, max_blocks_per_seq);
   if (batch == 0) return PKV_OK;
-  if (!q || !context_lens || !out)
-    return fail(PKV_ERR_INVALID, "null q, context_lens or out with batch = %d", batch);
-  if (max_context_len > 0 && (!k_cache || !v_cache || !block_tables || num_blocks == 0))
-    return fail(PKV_ERR_INVALID, "null cache or block table (or no blocks) with max_context_len = %d",
-                max_context_len);
-  if (!aligned16(q) || !aligned16(out) || !aligned16(k_cache) || !aligned16(v_cache))
-    return fail(PKV_ERR_INVALID, "q, out, k_cache and v_cache must be 16-byte aligned");
-  if ((st = check_stride("q_token_stride", q_token_stride, (int64_t)num_q_heads * head_dim, eb)) !=
-      PKV_OK)
-    return st;
-  if (!(scale == scale)) return fail(PKV_ERR_INVALID, "scale is NaN");
-  pkv::DecodePlan plan;
-  if (!pkv::plan_decode(batch, num_q_heads, num_kv_heads, max_context_len, num_splits, &plan))
+  if (!context_lens || !out)
+    return fail(PKV_ERR_INVALID, "null context_lens or out with batch = %d", batch);
+  if (!aligned16(out)) return fail(PKV_ERR_INVALID, "out must be 16-byte aligned");
+  if (!pkv::plan_decode(batch, num_q_heads, num_kv_heads, max_context_len, num_splits, plan))
     return fail(PKV_ERR_UNSUPPORTED, "no decode plan for these arguments");
-  if (workspace_bytes < plan.workspace_bytes || (plan.workspace_bytes && !workspace))
+  if (workspace_bytes < plan->workspace_bytes || (plan->workspace_bytes && !workspace))
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
-                workspace ? workspace_bytes : (size_t)0, plan.workspace_bytes);
-  if (plan.workspace_bytes && !aligned16(workspace))
+                workspace ? workspace_bytes : (size_t)0, plan->workspace_bytes);
+  if (plan->workspace_bytes && !aligned16(workspace))
     return fail(PKV_ERR_INVALID, "workspace must be 16-byte aligned");
+  return PKV_OK;
+}
+
+pkv_status decode_parts(int parts, pkv_dtype dtype, const void* q, int64_t q_token_stride,
+                        const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                        int32_t max_blocks_per_seq, const int32_t* context_lens,
+                        int32_t max_context_len, int32_t batch, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                        int64_t num_blocks, float scale, int32_t num_splits, void* out,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (eb == 0) return fail(PKV_ERR_INVALID, "unknown dtype %d", (int)dtype);
+  pkv_status st = check_geometry(num_q_heads, num_kv_heads, head_dim, block_size);
+  if (st != PKV_OK) return st;
+  if (parts & kSplitOnly) {
+    if (max_blocks_per_seq < 0 || num_blocks < 0)
+      return fail(PKV_ERR_INVALID, "max_blocks_per_seq and num_blocks must be >= 0");
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+      return fail(PKV_ERR_INVALID, "max_context_len (%d) > max_blocks_per_seq (%d) * block_size",
+                  max_context_len, max_blocks_per_seq);
+  }
+  pkv::DecodePlan plan;
+  st = check_decode_common(dtype, batch, num_q_heads, num_kv_heads, head_dim,
+                                      block_size, max_context_len, num_splits, context_lens, out,
+                                      workspace, workspace_bytes, &plan);
+  if (st != PKV_OK || batch == 0) return st;
+  if (parts & kSplitOnly) {
+    if (!q) return fail(PKV_ERR_INVALID, "null q with batch = %d", batch);
+    if (max_context_len > 0 && (!k_cache || !v_cache || !block_tables || num_blocks == 0))
+      return fail(PKV_ERR_INVALID,
+                  "null cache or block table (or no blocks) with max_context_len = %d",
+                  max_context_len);
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+      return fail(PKV_ERR_INVALID, "q, k_cache and v_cache must be 16-byte aligned");
+    if ((st = check_stride("q_token_stride", q_token_stride, (int64_t)num_q_heads * head_dim,
+                           eb)) != PKV_OK)
+      return st;
+    if (!(scale == scale)) return fail(PKV_ERR_INVALID, "scale is NaN");
+  }
   pkv::DecodeLaunch l;
   l.q = q;
   l.q_stride = q_token_stride;
@@ -188,7 +218,58 @@ pkv_status pkv_paged_decode(pkv_dtype dtype, const void* q, int64_t q_token_stri
   l.scale = scale;
   l.out = out;
   l.workspace = plan.workspace_bytes ? (float*)workspace : nullptr;
-  return hip_status(pkv::launch_decode(eb, plan, l, (hipStream_t)stream), "paged_decode launch");
+  if (parts & kSplitOnly) {
+    st = hip_status(pkv::launch_decode_split(eb, plan, l, (hipStream_t)stream),
+                    "paged_decode split launch");
+    if (st != PKV_OK) return st;
+  }
+  if (parts & kMergeOnly)
+    st = hip_status(pkv::launch_decode_merge(eb, plan, l, (hipStream_t)stream),
+                    "paged_decode merge launch");
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_paged_decode(pkv_dtype dtype, const void* q, int64_t q_token_stride,
+                            const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t max_context_len, int32_t batch,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int64_t num_blocks, float scale,
+                            int32_t num_splits, void* out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return decode_parts(kSplitAndMerge, dtype, q, q_token_stride, k_cache, v_cache, block_tables,
+                      max_blocks_per_seq, context_lens, max_context_len, batch, num_q_heads,
+                      num_kv_heads, head_dim, block_size, num_blocks, scale, num_splits, out,
+                      workspace, workspace_bytes, stream);
+}
+
+pkv_status pkv_paged_decode_partials(pkv_dtype dtype, const void* q, int64_t q_token_stride,
+                                     const void* k_cache, const void* v_cache,
+                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* context_lens, int32_t max_context_len,
+                                     int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                     float scale, int32_t num_splits, void* out, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  return decode_parts(kSplitOnly, dtype, q, q_token_stride, k_cache, v_cache, block_tables,
+                      max_blocks_per_seq, context_lens, max_context_len, batch, num_q_heads,
+                      num_kv_heads, head_dim, block_size, num_blocks, scale, num_splits, out,
+                      workspace, workspace_bytes, stream);
+}
+
+pkv_status pkv_paged_decode_merge(pkv_dtype dtype, const int32_t* context_lens,
+                                  int32_t max_context_len, int32_t batch, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t num_splits, void* out, const void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return decode_parts(kMergeOnly, dtype, nullptr, 0, nullptr, nullptr, nullptr, 0, context_lens,
+                      max_context_len, batch, num_q_heads, num_kv_heads, head_dim, block_size, 0,
+                      1.0f, num_splits, out, const_cast<void*>(workspace), workspace_bytes,
+                      stream);
 }
 
 pkv_status pkv_paged_prefill_varlen(pkv_dtype dtype, const void* q, int64_t q_token_stride,

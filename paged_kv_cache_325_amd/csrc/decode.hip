@@ -322,11 +322,17 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
-// Merge the split partials of one (sequence, query head) per wavefront, in
-// split order: M = max_s m_s, out = sum_s 2^(m_s-M) acc_s / sum_s 2^(m_s-M) l_s.
-// Sequences with a single split were finished by the split kernel.
+// Merge the split partials of one (sequence, query head) per wavefront:
+// M = max_s m_s, out = sum_s 2^(m_s-M) acc_s / sum_s 2^(m_s-M) l_s, with the
+// acc sum taken in split order.  The kernel is latency-bound (a few KB per
+// wavefront), so every load is issued before the first use: lane s fetches
+// split s's (m, l), and the acc rows of 16 splits are in flight while the
+// maximum is reduced.  Splits beyond 64 (very long contexts with small
+// splits) go through the general loop.  Sequences with a single split were
+// finished by the split kernel.
 template <int kElemBytes>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+  constexpr int kBatch = 16;
   const int lane = threadIdx.x & 63;
   const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (pair >= a.batch * a.num_q_heads) return;
@@ -335,18 +341,49 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   const int ns = (n + a.split_tokens - 1) / a.split_tokens;
   if (ns <= 1) return;
   const int64_t base = (int64_t)pair * a.nsplit;
-  float M = -INFINITY;
-  for (int t = 0; t < ns; ++t) M = fmaxf(M, a.ws_ml[(base + t) * 2]);
-  float L = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int t = 0; t < ns; ++t) {
-    const f32x2 ml = *reinterpret_cast<const f32x2*>(a.ws_ml + (base + t) * 2);
-    const float f = fast_exp2(ml[0] - M);
-    L = fmaf(f, ml[1], L);
-    const f32x2 v = *reinterpret_cast<const f32x2*>(a.ws_acc + (base + t) * kHeadDim + lane * 2);
-    o0 = fmaf(f, v[0], o0);
-    o1 = fmaf(f, v[1], o1);
+  const float* acc_rows = a.ws_acc + base * kHeadDim + lane * 2;
+
+  // first group: (m, l) of splits 0..63 and acc rows of splits 0..15
+  f32x2 ml = f32x2{-INFINITY, 0.f};
+  if (lane < ns) ml = *reinterpret_cast<const f32x2*>(a.ws_ml + (base + lane) * 2);
+  f32x2 v[kBatch];
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j)  // past the end: a valid row with weight 0
+    v[j] = *reinterpret_cast<const f32x2*>(acc_rows + (int64_t)min(j, ns - 1) * kHeadDim);
+
+  float M = ml[0];
+  for (int g0 = 64; g0 < ns; g0 += 64) {
+    const int t = g0 + lane;
+    M = fmaxf(M, t < ns ? a.ws_ml[(base + t) * 2] : -INFINITY);
   }
-  const float inv = 1.0f / L;
+  M = wave_max(M);
+
+  float l_lane = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int g0 = 0; g0 < ns; g0 += 64) {
+    if (g0 > 0) {
+      const int t = g0 + lane;
+      ml = t < ns ? *reinterpret_cast<const f32x2*>(a.ws_ml + (base + t) * 2)
+                  : f32x2{-INFINITY, 0.f};
+    }
+    const float f = fast_exp2(ml[0] - M);  // 0 for lanes past the end
+    l_lane = fmaf(f, ml[1], l_lane);
+    const int gn = min(64, ns - g0);
+    for (int j0 = 0; j0 < gn; j0 += kBatch) {
+      if (g0 > 0 || j0 > 0) {
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+          v[j] = *reinterpret_cast<const f32x2*>(
+              acc_rows + (int64_t)(g0 + min(j0 + j, gn - 1)) * kHeadDim);
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const float fj = j0 + j < gn ? lane_value(f, j0 + j) : 0.f;
+        o0 = fmaf(fj, v[j][0], o0);
+        o1 = fmaf(fj, v[j][1], o1);
+      }
+    }
+  }
+  const float inv = 1.0f / wave_sum(l_lane);
   constexpr int kRowBytes = kHeadDim * kElemBytes;
   if constexpr (kElemBytes == 2) {
     reinterpret_cast<uint32_t*>(a.out + (int64_t)pair * kRowBytes)[lane] =
@@ -415,8 +452,7 @@ bool plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_context_l
   return true;
 }
 
-hipError_t launch_decode(int elem_bytes, const DecodePlan& plan, const DecodeLaunch& l,
-                         hipStream_t stream) {
+static DecodeArgs decode_args(int elem_bytes, const DecodePlan& plan, const DecodeLaunch& l) {
   DecodeArgs a;
   a.q = (const uint8_t*)l.q;
   a.q_stride_bytes = l.q_stride * elem_bytes;
@@ -438,17 +474,26 @@ hipError_t launch_decode(int elem_bytes, const DecodePlan& plan, const DecodeLau
   a.ws_ml = l.workspace
                 ? l.workspace + (size_t)l.batch * l.num_q_heads * plan.nsplit * kHeadDim
                 : nullptr;
+  return a;
+}
 
-  const int64_t grid =
-      (int64_t)plan.nsplit * l.batch * l.num_kv_heads * plan.head_chunks;
+hipError_t launch_decode_split(int elem_bytes, const DecodePlan& plan, const DecodeLaunch& l,
+                               hipStream_t stream) {
+  const DecodeArgs a = decode_args(elem_bytes, plan, l);
+  const int64_t grid = (int64_t)plan.nsplit * l.batch * l.num_kv_heads * plan.head_chunks;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (elem_bytes == 2)
     launch_split_heads<2>(plan.heads_per_wg, a, (unsigned)grid, stream);
   else
     launch_split_heads<4>(plan.heads_per_wg, a, (unsigned)grid, stream);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || plan.nsplit <= 1) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(int elem_bytes, const DecodePlan& plan, const DecodeLaunch& l,
+                               hipStream_t stream) {
+  if (plan.nsplit <= 1 || l.batch <= 0) return hipSuccess;  // nothing was split
+  const DecodeArgs a = decode_args(elem_bytes, plan, l);
   const int64_t pairs = (int64_t)l.batch * l.num_q_heads;
   const unsigned mgrid = (unsigned)((pairs + 3) / 4);
   if (elem_bytes == 2)

@@ -46,8 +46,14 @@ struct DecodeLaunch {
   float* workspace;
 };
 
-hipError_t launch_decode(int elem_bytes, const DecodePlan& plan, const DecodeLaunch& a,
-                         hipStream_t stream);
+// The split kernel (partials, and outputs of single-split sequences) and the
+// merge kernel (outputs of split sequences).  Only q, caches, tables and
+// scale are used by the split launch; the merge uses context_lens, batch,
+// head counts, out and workspace.
+hipError_t launch_decode_split(int elem_bytes, const DecodePlan& plan, const DecodeLaunch& a,
+                               hipStream_t stream);
+hipError_t launch_decode_merge(int elem_bytes, const DecodePlan& plan, const DecodeLaunch& a,
+                               hipStream_t stream);
 
 // ---- varlen causal prefill ----------------------------------------------
 bool prefill_supported_group(int group);

@@ -153,3 +153,24 @@ def test_binding_refuses_cpu_tensors():
     s = torch.zeros(4, dtype=torch.int32)
     with pytest.raises(ValueError):
         pkv.pkv_kv_store(x, x, c, c, s)
+
+
+def _merge(**kw):
+    a = dict(dtype=BF16, ctx=FAKE, maxctx=4096, batch=4, hq=16, hkv=8, d=128, bs=256, splits=4,
+             out=FAKE, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    lib = pkv.load_library()
+    return lib.pkv_paged_decode_merge(a["dtype"], a["ctx"], a["maxctx"], a["batch"], a["hq"],
+                                      a["hkv"], a["d"], a["bs"], a["splits"], a["out"], a["ws"],
+                                      a["wsb"], None)
+
+
+def test_merge_errors():
+    assert _merge(batch=0) == OK
+    assert _merge(ctx=None) == INVALID
+    assert _merge(out=None) == INVALID
+    assert _merge(ws=None, wsb=0) == WORKSPACE
+    assert _merge(d=64) == UNSUPPORTED
+    assert _merge(hq=24) == UNSUPPORTED
+    assert _merge(splits=-1) == INVALID
+    assert _merge(dtype=9) == INVALID

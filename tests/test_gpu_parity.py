@@ -114,6 +114,69 @@ def test_split_partials_in_workspace():
     assert_close(out2.double().cpu().numpy(), expected(w), "reused workspace")
 
 
+def test_merge_of_oracle_partials():
+    """The merge entry point alone: fed the oracle's split partials (written
+    into the documented workspace layout), it must produce the oracle's
+    merged output."""
+    w = build([s for s in SMALL if s.name == "dec-bf16-g4-long"][0])
+    splits = 5
+    args = (w.batch, w.num_q_heads, w.num_kv_heads, 128, w.max_context_len, 256, splits)
+    S = pkv.pkv_paged_decode_split_tokens(*args)
+    ns = -(-w.max_context_len // S)
+    kcb, vcb = stored_bits(w)
+    kc, vc = ref.widen(kcb, w.dtype), ref.widen(vcb, w.dtype)
+    q = q64(w)
+    parts = ref.decode_partials(q, kc, vc, w.block_tables, w.context_lens, w.scale, S)
+    acc = np.zeros((w.batch, w.num_q_heads, ns, 128), np.float32)
+    ml = np.zeros((w.batch, w.num_q_heads, ns, 2), np.float32)
+    log2e = 1.0 / math.log(2.0)
+    want = np.zeros((w.batch, w.num_q_heads, 128))
+    merged_rows = []
+    for b, (pacc, pm, pl) in enumerate(parts):
+        nsb = pacc.shape[0]
+        if nsb <= 1:
+            continue
+        merged_rows.append(b)
+        acc[b, :, :nsb] = pacc.transpose(1, 0, 2)
+        ml[b, :, :nsb, 0] = (pm * log2e).T
+        ml[b, :, :nsb, 1] = pl.T
+        want[b] = ref.merge_partials(pacc, pm, pl)
+    assert merged_rows, "the case must split some sequences"
+    nbytes = pkv.pkv_paged_decode_workspace_bytes(*args)
+    host = np.concatenate([acc.ravel(), ml.ravel()])
+    assert host.size * 4 == nbytes
+    ws = torch.from_numpy(host).cuda()
+    out = torch.full((w.batch, w.num_q_heads, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ctx = torch.from_numpy(w.context_lens).cuda()
+    announce("merge of oracle partials")
+    pkv.pkv_paged_decode_merge(ctx, w.max_context_len, w.num_q_heads, w.num_kv_heads, out, ws,
+                               num_splits=splits)
+    torch.cuda.synchronize()
+    got = out.double().cpu().numpy()
+    assert_close(got[merged_rows], want[merged_rows], "merge")
+    # rows of single-split sequences are not touched by the merge
+    others = [b for b in range(w.batch) if b not in merged_rows]
+    assert torch.isnan(out[others].float()).all()
+
+
+def test_partials_then_merge_equals_decode_bit_exact():
+    w = build([s for s in SMALL if s.name == "dec-bf16-g2-ragged"][0])
+    d = to_device(w)
+    check_inputs(d)
+    store(d)
+    announce("decode in one call")
+    whole = pkv.pkv_paged_decode(d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens,
+                                 w.max_context_len, w.scale, num_splits=6)
+    announce("decode in two calls")
+    out, ws = pkv.pkv_paged_decode_partials(d.q, d.k_cache, d.v_cache, d.block_tables,
+                                            d.context_lens, w.max_context_len, w.scale,
+                                            num_splits=6)
+    pkv.pkv_paged_decode_merge(d.context_lens, w.max_context_len, w.num_q_heads,
+                               w.num_kv_heads, out, ws, num_splits=6)
+    torch.cuda.synchronize()
+    assert torch.equal(whole.view(torch.int16), out.view(torch.int16))
+
+
 # ---------------------------------------------------------------------------
 # invariants on the GPU result
 # ---------------------------------------------------------------------------
