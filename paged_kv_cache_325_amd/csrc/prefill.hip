@@ -14,7 +14,8 @@
 // the softmax row max/sum is in-lane plus one exchange with lane l^32, and
 // the probabilities come out of the accumulator already in the layout the
 // next MFMA wants as its B operand.  Output is accumulated transposed too,
-// O^T += V^T * P^T, with V^T staged in LDS.
+// O^T += V^T * P^T; the V^T operand is read straight from the natural V tile
+// with the LDS transpose read (ds_read_b64_tr_b16).
 //
 // Work decomposition.  A workgroup is 4 wavefronts and owns one kv head g of
 // one sequence and 4 "query tiles" of 32 rows: 4 query heads of g's group
@@ -22,16 +23,15 @@
 // or 1 head x 128 positions (group 1).  The 4 waves share every K/V tile the
 // workgroup stages, so each K/V byte is fetched once per 128 query rows.
 // Keys are processed in tiles of 64 (a tile never crosses a 256-token block,
-// so one block-table lookup per tile), with the next tile prefetched into
-// registers while the current one is consumed.  Workgroups are ordered
+// so one block-table lookup per tile).  Workgroups are ordered
 // last-query-tile first (most keys first), and consecutive workgroup ids
 // differ in kv head, so with 8 kv heads all tiles of one (sequence, kv head)
 // land on the same XCD and share its L2.
 //
-// LDS: K tile [64 keys][16 x 16 B], column c of key r at c ^ (r & 15);
-//      V^T tile [128 dims][64 keys] with a key order and swizzle described
-//      at vt_offset.  Both layouts keep the MFMA operand reads and the
-//      staging writes free of LDS bank conflicts.  32 KiB per workgroup.
+// Staging.  K and V tiles are copied global -> LDS with the direct-to-LDS
+// buffer load (no registers, no VALU), double-buffered: the copy of tile
+// t+1 is in flight while tile t is consumed.  64 KiB of LDS per workgroup,
+// two workgroups per CU.
 //
 // Softmax work per tile is kept small because it competes with the MFMAs
 // for issue slots: the causal mask is a select, the scale is folded into
@@ -46,9 +46,7 @@ namespace pkv {
 
 namespace {
 
-// 32-query column blocks per wave.  One block (two waves per SIMD) measured
-// faster than two (one wave per SIMD, accumulators spilling into AGPR moves).
-constexpr int kWaveCB = 1;
+constexpr int kQT = 32;  // query rows per wave
 constexpr int kKT = 64;                  // keys per tile
 constexpr int kThreads = 256;
 
@@ -71,33 +69,40 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
 
-// V^T tile in LDS: 128 rows (dims) x 64 keys of bf16, 128 bytes per row, in
-// 8-byte units.  Keys are stored so that the 8 keys one lane feeds to a PV
-// MFMA -- kt*32 + 16ks + 4hf + {0..3} and the same + 8, the order in which
-// the S^T accumulator hands out probabilities -- are 16 contiguous bytes:
-// within each 16-key group the two bits above the 4-key group are swapped.
-// The 16-byte column is XOR-swizzled with ((d >> 1) + (d >> 4)) & 7, which
-// (with the staging lane map) keeps both the b64 writes and the b128 reads
-// free of bank conflicts.
-__device__ __forceinline__ int vt_swizzle(int d) { return ((d >> 1) + (d >> 4)) & 7; }
-// 8-byte slot of the 4-key group q (keys 4q .. 4q+3) in row d
-__device__ __forceinline__ int vt_offset(int d, int q) {
-  const int qp = (q & ~3) | ((q & 1) << 1) | ((q >> 1) & 1);
-  return d * 16 + (((qp >> 1) ^ vt_swizzle(d)) << 1) + (qp & 1);
-}
-// first 8-byte slot of the (permuted) 16-byte chunk c16 of row d
-__device__ __forceinline__ int vt_offset_chunk(int d, int c16) {
-  return d * 16 + ((c16 ^ vt_swizzle(d)) << 1);
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// K and V tiles live in LDS in their natural [64 keys][128 dims] bf16 order,
+// 256 bytes per key row, with the 16-byte chunks of row `key` permuted:
+//   K: chunk c at position c ^ (key & 15)
+//   V: chunk c at position c ^ (2 * (key & 7))   (32-byte blocks permuted)
+// so that the MFMA operand reads below hit distinct LDS banks.  Tiles are
+// copied global -> LDS by the direct-to-LDS load (no registers, no VALU):
+// lane l of a wave instruction lands at LDS base + 16 l, so each lane fetches
+// the global chunk that belongs at that position.
+__device__ __forceinline__ int k_pos(int key, int c) { return c ^ (key & 15); }
+__device__ __forceinline__ int v_pos(int key, int c) { return c ^ ((key & 7) << 1); }
+
+// Copy one 64-key tile (K or V, rows k0 .. k0+63 of a (block, kv head)) into
+// LDS: each of the 4 waves moves 16 keys, 1 KiB per instruction.
+template <bool kIsV>
+__device__ __forceinline__ void tile_to_lds(const uint16_t* rows, u32x4* lds, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int key = wave * 16 + i * 4 + (lane >> 4);
+    const int pos = lane & 15;
+    const int c = kIsV ? v_pos(key, pos) : k_pos(key, pos);  // the involution maps back
+    __builtin_amdgcn_global_load_lds(rows + key * kHeadDim + c * 8,
+                                     (lds_void*)(lds + (wave * 16 + i * 4) * 16), 16, 0, 0);
+  }
 }
 
-// kCB column blocks of 32 queries per wave (64 queries for kCB = 2): the
-// K and V^T operands read from LDS are shared by the column blocks, and one
-// block's softmax (VALU) can overlap the other block's MFMAs.
-template <int kCB>
-__global__ __launch_bounds__(kThreads, kCB == 1 ? 2 : 1) void prefill_kernel(PrefillArgs a) {
-  constexpr int kQT = 32 * kCB;  // query rows per wave
-  __shared__ u32x4 k_lds[kKT * 16];      // 16 KiB
-  __shared__ __attribute__((aligned(16))) u32x2 vt_lds[kHeadDim * 16];  // 16 KiB
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
+  // Double-buffered K and V tiles (two named buffers, so the compiler can
+  // tell the tile being read from the tile being copied in).  64 KiB.
+  __shared__ u32x4 k_lds0[kKT * 16], k_lds1[kKT * 16];
+  __shared__ u32x4 v_lds0[kKT * 16], v_lds1[kKT * 16];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -130,194 +135,177 @@ __global__ __launch_bounds__(kThreads, kCB == 1 ? 2 : 1) void prefill_kernel(Pre
   const int my_kend = max(0, min(n_k, off + min(n_q, my_q0 + kQT)));
   const int ntiles = (wg_kend + kKT - 1) / kKT;
 
-  // this lane's query column in block cb: row qi[cb] (clamped for loads)
-  int qi[kCB], q_pos[kCB];
-  u32x4 qreg[kCB][8];
-#pragma unroll
-  for (int cb = 0; cb < kCB; ++cb) {
-    qi[cb] = my_q0 + cb * 32 + j;
-    q_pos[cb] = off + qi[cb];  // last visible key of this query
-    const int q_row = q_begin + min(qi[cb], max(n_q - 1, 0));
+  // this lane's query column: row qi of the sequence (clamped for loads)
+  const int qi = my_q0 + j;
+  const int q_pos = off + qi;  // last visible key of this query
+  u32x4 qreg[8];
+  {
+    const int q_row = q_begin + min(qi, max(n_q - 1, 0));
     const uint16_t* qp = a.q + (int64_t)q_row * a.q_stride + (int64_t)h * kHeadDim + hf * 8;
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) qreg[cb][kb] = *reinterpret_cast<const u32x4*>(qp + kb * 16);
+    for (int kb = 0; kb < 8; ++kb) qreg[kb] = *reinterpret_cast<const u32x4*>(qp + kb * 16);
   }
 
-  f32x16 o_acc[kCB][4];
-  float m_run[kCB], l_part[kCB];
+  f32x16 o_acc[4];
 #pragma unroll
-  for (int cb = 0; cb < kCB; ++cb) {
-#pragma unroll
-    for (int db = 0; db < 4; ++db) o_acc[cb][db] = f32x16{};
-    m_run[cb] = -INFINITY;
-    l_part[cb] = 0.f;
-  }
+  for (int db = 0; db < 4; ++db) o_acc[db] = f32x16{};
+  float m_run = -INFINITY;
+  float l_part = 0.f;
+  const float c = a.scale_log2;
 
   const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
-  // Staging assignment.  K: chunk (key tid/16 + 16 i, 16-byte column tid%16).
-  // V: the four keys vkrow*4 .. +3 of 16-byte column vcol (8 dims); the
-  // lane -> (vcol, vkrow) bit mapping makes the transposed LDS writes
-  // conflict-free (see vt_offset).
-  const int col = tid & 15;
-  const int krow = tid >> 4;
-  const int vcol = (lane & 7) | (((lane >> 4) & 1) << 3);
-  const int vkrow = wave * 4 + (((lane >> 5) & 1) | (((lane >> 3) & 1) << 1));
-  u32x4 kpre[4], vpre[4];
-
-  auto prefetch = [&](int t) {
+  auto issue_copy = [&](int t, u32x4* kbuf, u32x4* vbuf) {
     const int k0 = t * kKT;
     const int64_t blk = table[k0 / kBlockSize];
     const int64_t base = ((blk * a.num_kv_heads + g) * kBlockSize + (k0 % kBlockSize)) * kHeadDim;
-    const uint16_t* kt = a.k_cache + base + col * 8;
-    const uint16_t* vt = a.v_cache + base + vcol * 8;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      kpre[i] = *reinterpret_cast<const u32x4*>(kt + (krow + 16 * i) * kHeadDim);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      vpre[i] = *reinterpret_cast<const u32x4*>(vt + (vkrow * 4 + i) * kHeadDim);
+    tile_to_lds<false>(a.k_cache + base, kbuf, wave, lane);
+    tile_to_lds<true>(a.v_cache + base, vbuf, wave, lane);
   };
 
-  auto stage = [&](int t) {
-    const int k0 = t * kKT;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = krow + 16 * i;
-      k_lds[key * 16 + (col ^ (key & 15))] = kpre[i];
-    }
-    // V rows past the context are zeroed: p = 0 there, and 0 * NaN poison
-    // inside an MFMA would still be NaN.
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (k0 + vkrow * 4 + i >= n_k) vpre[i] = u32x4{0u, 0u, 0u, 0u};
-    // transpose: dim d = vcol*8 + e receives keys vkrow*4 .. +3
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      // dims 2w (low halves) and 2w+1 (high halves) of the four keys
-      const uint32_t lo01 = __builtin_amdgcn_perm(vpre[1][w], vpre[0][w], 0x05040100u);
-      const uint32_t lo23 = __builtin_amdgcn_perm(vpre[3][w], vpre[2][w], 0x05040100u);
-      const uint32_t hi01 = __builtin_amdgcn_perm(vpre[1][w], vpre[0][w], 0x07060302u);
-      const uint32_t hi23 = __builtin_amdgcn_perm(vpre[3][w], vpre[2][w], 0x07060302u);
-      const int d0 = vcol * 8 + 2 * w;
-      vt_lds[vt_offset(d0, vkrow)] = u32x2{lo01, lo23};
-      vt_lds[vt_offset(d0 + 1, vkrow)] = u32x2{hi01, hi23};
-    }
+  // PV operand reads (ds_read_b64_tr_b16): in each 16-lane group, lane
+  // 4a+e receives element e of the 8-byte chunks addressed by lanes a, a+4,
+  // a+8, a+12.  Lane (G = lane/16, a = lane%4, m = (lane%16)/4) therefore
+  // addresses key kt*32 + 16ks + 4hf + m (+8 for the second half) at dims
+  // 32db + 16(G%2) + 4a: the lane then holds, for dim 32db + lane%32, the
+  // four keys in the order the S^T accumulator produced the probabilities.
+  const int tr_g = lane >> 4;
+  const int tr_a = lane & 3;
+  const int tr_m = (lane >> 2) & 3;
+  auto tr_read = [&](const u32x4* vbuf, int key, int dim) -> uint64_t {
+    const int cpos = v_pos(key, dim >> 3);
+    const char* p = reinterpret_cast<const char*>(vbuf) + key * 256 + cpos * 16 + (dim & 7) * 2;
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+    return __builtin_bit_cast(uint64_t, v);
   };
 
-  const float c = a.scale_log2;
-  if (ntiles > 0) prefetch(0);
-  for (int t = 0; t < ntiles; ++t) {
-    if (t > 0) __syncthreads();
-    stage(t);
-    __syncthreads();
-    if (t + 1 < ntiles) prefetch(t + 1);
+  auto tile = [&](int t, const u32x4* kbuf, u32x4* vbuf) {
     const int k0 = t * kKT;
-    if (!wave_has_rows || k0 >= my_kend) continue;
+    if (!wave_has_rows || k0 >= my_kend) return;  // uniform over the wave
 
-    // ---- S^T = K Q^T for 2 x 32 keys and every column block ---------------
-    f32x16 s_acc[kCB][2];
+    // ---- S^T = K Q^T for 2 x 32 keys ------------------------------------
+    f32x16 s_acc[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int key = kt * 32 + j;
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb) {
-        const u32x4 av = k_lds[key * 16 + ((kb * 2 + hf) ^ (key & 15))];
-#pragma unroll
-        for (int cb = 0; cb < kCB; ++cb)
-          s_acc[cb][kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              as_bf16x8(av), as_bf16x8(qreg[cb][kb]), kb == 0 ? f32x16{} : s_acc[cb][kt], 0, 0, 0);
+        const u32x4 av = kbuf[key * 16 + k_pos(key, kb * 2 + hf)];
+        s_acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(av), as_bf16x8(qreg[kb]), kb == 0 ? f32x16{} : s_acc[kt], 0, 0, 0);
       }
     }
 
-    // ---- online softmax (base 2), one column block at a time --------------
-    // element e = rr*4 + ee of s_acc[cb][kt] is key k0 + kt*32 + 8*rr + 4*hf + ee.
-    const bool diag = (k0 + kKT - 1 > off + my_q0) || (k0 + kKT > n_k);
-    u32x4 pfrag[kCB][4];  // B operands: (kt, ks) -> 16 keys
-#pragma unroll
-    for (int cb = 0; cb < kCB; ++cb) {
-      if (diag) {  // masked keys (past the query's position or the context) -> -inf
-        const int lim = min(q_pos[cb], n_k - 1) - k0 - 4 * hf;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int ko = kt * 32 + 8 * (e >> 2) + (e & 3);
-            s_acc[cb][kt][e] = ko <= lim ? s_acc[cb][kt][e] : -INFINITY;
-          }
-      }
-      float tmax = -INFINITY;
+    // ---- online softmax (base 2) ------------------------------------------
+    // element e = rr*4 + ee of s_acc[kt] is key k0 + kt*32 + 8*rr + 4*hf + ee
+    if ((k0 + kKT - 1 > off + my_q0) || (k0 + kKT > n_k)) {
+      // masked keys (past the query's position or the context) -> -inf
+      const int lim = min(q_pos, n_k - 1) - k0 - 4 * hf;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int e = 0; e < 16; e += 2)
-          tmax = fmaxf(tmax, fmaxf(s_acc[cb][kt][e], s_acc[cb][kt][e + 1]));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * c;  // both lane halves hold the query
-      // Lazy rescaling: the running max only moves (and O, l are rescaled)
-      // when a score exceeds it by more than kRescaleSlack (log2 units), so
-      // p <= 2^kRescaleSlack stays well inside fp32/bf16 range.
-      const bool grow = tmax > m_run[cb] + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        const float m_new = grow ? tmax : m_run[cb];
-        const float alpha = grow ? fast_exp2(m_run[cb] - m_new) : 1.f;  // 0 when leaving -inf
-        m_run[cb] = m_new;
-        l_part[cb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) o_acc[cb][db] *= alpha;
-      }
-      const float neg_m = m_run[cb] == -INFINITY ? 0.f : -m_run[cb];
-      float psum = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          float p[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(s_acc[cb][kt][ks * 8 + e], c, neg_m));
-          psum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-          pfrag[cb][kt * 2 + ks] = u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]),
-                                         pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])};
+        for (int e = 0; e < 16; ++e) {
+          const int ko = kt * 32 + 8 * (e >> 2) + (e & 3);
+          s_acc[kt][e] = ko <= lim ? s_acc[kt][e] : -INFINITY;
         }
-      l_part[cb] += psum;
     }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) tmax = fmaxf(tmax, fmaxf(s_acc[kt][e], s_acc[kt][e + 1]));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * c;  // both lane halves hold the query
+    // Lazy rescaling: the running max only moves (and O, l are rescaled)
+    // when a score exceeds it by more than kRescaleSlack (log2 units), so
+    // p <= 2^kRescaleSlack stays well inside fp32/bf16 range.
+    const bool grow = tmax > m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? tmax : m_run;
+      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;  // 0 when leaving -inf
+      m_run = m_new;
+      l_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o_acc[db] *= alpha;
+    }
+    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+    float psum = 0.f;
+    u32x4 pfrag[4];  // B operands: (kt, ks) -> 16 keys
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(s_acc[kt][ks * 8 + e], c, neg_m));
+        psum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        pfrag[kt * 2 + ks] = u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]),
+                                   pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])};
+      }
+    l_part += psum;
 
     // ---- O^T += V^T P^T ------------------------------------------------------
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      const int d = db * 32 + j;
+      const int dim = db * 32 + 16 * (tr_g & 1) + 4 * tr_a;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          // keys kt*32 + 16ks + 4hf + {0..3} and the same + 8, in one 16 bytes
-          const u32x4 av = *reinterpret_cast<const u32x4*>(
-              &vt_lds[vt_offset_chunk(d, kt * 4 + ks * 2 + hf)]);
-#pragma unroll
-          for (int cb = 0; cb < kCB; ++cb)
-            o_acc[cb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                as_bf16x8(av), as_bf16x8(pfrag[cb][kt * 2 + ks]), o_acc[cb][db], 0, 0, 0);
+          const int key = kt * 32 + ks * 16 + 4 * hf + tr_m;
+          const uint64_t lo = tr_read(vbuf, key, dim);
+          const uint64_t hi = tr_read(vbuf, key + 8, dim);
+          const u32x4 av = u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi,
+                                 (uint32_t)(hi >> 32)};
+          o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              as_bf16x8(av), as_bf16x8(pfrag[kt * 2 + ks]), o_acc[db], 0, 0, 0);
         }
     }
+  };
+
+  // V rows past the context (only in the last tile) are zeroed in LDS once
+  // the tile has arrived: p = 0 there, but 0 * NaN poison inside an MFMA
+  // would still be NaN.
+  auto clear_tail = [&](int t, u32x4* vbuf) {
+    const int k0 = t * kKT;
+    if (k0 + kKT <= n_k) return;  // uniform over the workgroup
+    for (int i = tid; i < kKT * 16; i += kThreads)
+      if (k0 + i / 16 >= n_k) vbuf[i] = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+  };
+
+  // Tiles alternate between buffer 0 (even t) and buffer 1 (odd t).  The
+  // copy of tile t+1 is issued before tile t is consumed; the barrier at the
+  // end of each step makes tile t+1 visible and frees tile t's buffer.
+  if (ntiles > 0) issue_copy(0, k_lds0, v_lds0);
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's copies landed
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    if (t + 1 < ntiles) issue_copy(t + 1, k_lds1, v_lds1);
+    clear_tail(t, v_lds0);
+    tile(t, k_lds0, v_lds0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+    if (t + 1 >= ntiles) break;
+    if (t + 2 < ntiles) issue_copy(t + 2, k_lds0, v_lds0);
+    clear_tail(t + 1, v_lds1);
+    tile(t + 1, k_lds1, v_lds1);
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
   }
 
   // ---- epilogue: out[q_row][h][d] = O^T[d][j] / l ---------------------------
-  if (!wave_has_rows) return;
+  if (!wave_has_rows || qi >= n_q) return;
+  const float l_tot = l_part + __shfl_xor(l_part, 32, 64);
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  uint16_t* op = a.out + ((int64_t)(q_begin + qi) * a.num_q_heads + h) * kHeadDim;
 #pragma unroll
-  for (int cb = 0; cb < kCB; ++cb) {
-    const float l_tot = l_part[cb] + __shfl_xor(l_part[cb], 32, 64);
-    if (qi[cb] >= n_q) continue;
-    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    uint16_t* op = a.out + ((int64_t)(q_begin + qi[cb]) * a.num_q_heads + h) * kHeadDim;
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int d = db * 32 + 8 * rr + 4 * hf;
-        const u32x2 w =
-            u32x2{pack_bf16(o_acc[cb][db][rr * 4] * inv, o_acc[cb][db][rr * 4 + 1] * inv),
-                  pack_bf16(o_acc[cb][db][rr * 4 + 2] * inv, o_acc[cb][db][rr * 4 + 3] * inv)};
-        *reinterpret_cast<u32x2*>(op + d) = w;
-      }
-  }
+    for (int rr = 0; rr < 4; ++rr) {
+      const int d = db * 32 + 8 * rr + 4 * hf;
+      const u32x2 w = u32x2{pack_bf16(o_acc[db][rr * 4] * inv, o_acc[db][rr * 4 + 1] * inv),
+                            pack_bf16(o_acc[db][rr * 4 + 2] * inv, o_acc[db][rr * 4 + 3] * inv)};
+      *reinterpret_cast<u32x2*>(op + d) = w;
+    }
 }
 
 }  // namespace
@@ -341,14 +329,14 @@ hipError_t launch_prefill(const PrefillLaunch& l, hipStream_t stream) {
   a.heads_per_wg = a.group >= 4 ? 4 : a.group;
   a.pos_tiles = 4 / a.heads_per_wg;
   a.head_chunks = a.group / a.heads_per_wg;
-  const int wg_rows = 32 * kWaveCB * a.pos_tiles;
+  const int wg_rows = kQT * a.pos_tiles;
   a.max_wg_tiles = (l.max_seqlen_q + wg_rows - 1) / wg_rows;
   a.scale_log2 = l.scale * kLog2e;
   a.out = (uint16_t*)l.out;
   const int64_t grid = (int64_t)a.max_wg_tiles * l.batch * l.num_kv_heads * a.head_chunks;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(prefill_kernel<kWaveCB>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
