@@ -35,8 +35,10 @@
 //
 // Softmax work per tile is kept small because it competes with the MFMAs
 // for issue slots: the causal mask is a select, the scale is folded into
-// the exponent's FMA, and O is only rescaled when some query's running max
-// grows by more than 2^8 (lazy rescaling).
+// the exponent's FMA, and the row max (and the rescaling of O) is only
+// computed on tiles whose probabilities against the current running max
+// would exceed 2^16 (lazy rescaling); the row sums use v_dot2 on the packed
+// bf16 probabilities.
 #include <math.h>
 
 #include "pkv_device.h"
@@ -65,7 +67,11 @@ struct PrefillArgs {
   uint16_t* out;
 };
 
-constexpr float kRescaleSlack = 8.0f;  // log2 units
+// Bound on the probabilities computed against a lagging running max (see
+// the softmax step): with p <= 2^16, O and l stay far inside fp32 range
+// for any context the cache can hold.
+constexpr float kLazyBound = 65536.0f;
+constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -84,18 +90,34 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 __device__ __forceinline__ int k_pos(int key, int c) { return c ^ (key & 15); }
 __device__ __forceinline__ int v_pos(int key, int c) { return c ^ ((key & 7) << 1); }
 
-// Copy one 64-key tile (K or V, rows k0 .. k0+63 of a (block, kv head)) into
-// LDS: each of the 4 waves moves 16 keys, 1 KiB per instruction.
+// Copy one 64-key tile (K or V, rows k0 .. k0+63 of a (block, kv head),
+// `rsrc` addressing its 16 KiB) into LDS: each of the 4 waves moves 16
+// keys, 1 KiB per instruction.  The per-lane byte offsets depend only on the
+// lane and wave, so they are computed once per kernel (tile_offsets) and a
+// new tile only changes the scalar buffer base.
 template <bool kIsV>
-__device__ __forceinline__ void tile_to_lds(const uint16_t* rows, u32x4* lds, int wave, int lane) {
+__device__ __forceinline__ void tile_offsets(uint32_t (&voff)[4], int wave, int lane) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int key = wave * 16 + i * 4 + (lane >> 4);
     const int pos = lane & 15;
     const int c = kIsV ? v_pos(key, pos) : k_pos(key, pos);  // the involution maps back
-    __builtin_amdgcn_global_load_lds(rows + key * kHeadDim + c * 8,
-                                     (lds_void*)(lds + (wave * 16 + i * 4) * 16), 16, 0, 0);
+    voff[i] = (uint32_t)(key * kHeadDim + c * 8) * 2u;
   }
+}
+
+__device__ __forceinline__ void tile_to_lds(__amdgpu_buffer_rsrc_t rsrc, const uint32_t (&voff)[4],
+                                            u32x4* lds, int wave) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + (wave * 16 + i * 4) * 16), 16,
+                                             voff[i], 0, 0, 0);
+}
+
+// Raw buffer resource over one 16 KiB K or V tile (word 3: 32-bit data
+// format, the value used for untyped buffer access on gfx9-family parts).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, kKT * kHeadDim * 2, 0x00020000);
 }
 
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
@@ -154,12 +176,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   const float c = a.scale_log2;
 
   const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
+  uint32_t k_off[4], v_off[4];
+  tile_offsets<false>(k_off, wave, lane);
+  tile_offsets<true>(v_off, wave, lane);
   auto issue_copy = [&](int t, u32x4* kbuf, u32x4* vbuf) {
     const int k0 = t * kKT;
     const int64_t blk = table[k0 / kBlockSize];
     const int64_t base = ((blk * a.num_kv_heads + g) * kBlockSize + (k0 % kBlockSize)) * kHeadDim;
-    tile_to_lds<false>(a.k_cache + base, kbuf, wave, lane);
-    tile_to_lds<true>(a.v_cache + base, vbuf, wave, lane);
+    tile_to_lds(tile_rsrc(a.k_cache + base), k_off, kbuf, wave);
+    tile_to_lds(tile_rsrc(a.v_cache + base), v_off, vbuf, wave);
   };
 
   // PV operand reads (ds_read_b64_tr_b16): in each 16-lane group, lane
@@ -208,38 +233,56 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
           s_acc[kt][e] = ko <= lim ? s_acc[kt][e] : -INFINITY;
         }
     }
-    float tmax = -INFINITY;
+    // Probabilities against the running max m_run (log2 units).  The row
+    // max is only computed when it is needed: while every p of this tile is
+    // at most 2^kLazyBound (checked through the row sum, since p >= 0) the
+    // reference m_run may lag the true max -- softmax is invariant to it --
+    // and O, l need no rescaling.  Otherwise (or on a query's first visible
+    // tile) m_run moves to the true running max and the tile is redone.
+    u32x4 pfrag[4];  // B operands: (kt, ks) -> 16 keys
+    float psum;
+    auto probs = [&](float neg_m) {
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int e = 0; e < 16; e += 2) tmax = fmaxf(tmax, fmaxf(s_acc[kt][e], s_acc[kt][e + 1]));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * c;  // both lane halves hold the query
-    // Lazy rescaling: the running max only moves (and O, l are rescaled)
-    // when a score exceeds it by more than kRescaleSlack (log2 units), so
-    // p <= 2^kRescaleSlack stays well inside fp32/bf16 range.
-    const bool grow = tmax > m_run + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float m_new = grow ? tmax : m_run;
-      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;  // 0 when leaving -inf
+        for (int ks = 0; ks < 2; ++ks) {
+          float p[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(s_acc[kt][ks * 8 + e], c, neg_m));
+          const u32x4 f = u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]),
+                                pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])};
+          pfrag[kt * 2 + ks] = f;
+          // row sum of the bf16 probabilities the PV product consumes
+#pragma unroll
+          for (int w = 0; w < 4; ++w) acc[w] = dot2_bf16(f[w], kOnesBf16x2, acc[w]);
+        }
+      psum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    };
+    bool rebase = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
+    if (!rebase) {
+      probs(-m_run);
+      rebase = __builtin_amdgcn_ballot_w64(!(psum <= kLazyBound)) != 0;
+    }
+    if (rebase) {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) tmax = fmaxf(tmax, fmaxf(s_acc[kt][e], s_acc[kt][e + 1]));
+      // both lane halves hold the same query: combine lanes l and l ^ 32
+      const u32x2 sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, tmax),
+                                                        __builtin_bit_cast(uint32_t, tmax), false, false);
+      tmax = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1])) * c;
+      const float m_new = fmaxf(m_run, tmax);
+      // alpha = 0 when leaving -inf; 1 while the query has seen no key yet
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
       m_run = m_new;
       l_part *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; ++db) o_acc[db] *= alpha;
+      probs(m_new == -INFINITY ? 0.f : -m_new);
     }
-    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
-    float psum = 0.f;
-    u32x4 pfrag[4];  // B operands: (kt, ks) -> 16 keys
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        float p[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(s_acc[kt][ks * 8 + e], c, neg_m));
-        psum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-        pfrag[kt * 2 + ks] = u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]),
-                                   pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])};
-      }
     l_part += psum;
 
     // ---- O^T += V^T P^T ------------------------------------------------------
