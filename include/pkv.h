@@ -221,8 +221,15 @@ pkv_status pkv_paged_decode_merge(pkv_dtype dtype, const int32_t* context_lens,
  *   causal         must be 1: query i of sequence b sits at position
  *                  n_k - n_q + i and sees keys 0 .. n_k - n_q + i
  *   out            device, [total_q][num_q_heads][head_dim], dense, bf16
+ *   workspace      device, >= pkv_paged_prefill_workspace_bytes() bytes,
+ *                  4-byte aligned, caller-owned: the work-queue counters of
+ *                  the persistent kernel.  It must be zero-filled before its
+ *                  first use; every call leaves it zero again when its
+ *                  kernel ends, so one fill at allocation suffices.  Calls
+ *                  that may run concurrently need distinct workspaces.
  * total_q = cu_seqlens_q[batch] is not passed; rows outside the ranges are
- * neither read nor written.
+ * neither read nor written.  PKV_ERR_WORKSPACE: workspace null, misaligned
+ * or too small.
  */
 pkv_status pkv_paged_prefill_varlen(
     pkv_dtype dtype, const void* q, int64_t q_token_stride,
@@ -231,7 +238,11 @@ pkv_status pkv_paged_prefill_varlen(
     const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t batch,
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
     int32_t block_size, int64_t num_blocks, float scale, int32_t causal,
-    void* out, void* stream);
+    void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* pkv_paged_prefill_workspace_bytes -- workspace size that
+ * pkv_paged_prefill_varlen needs (independent of the problem size). */
+size_t pkv_paged_prefill_workspace_bytes(void);
 
 /*
  * pkv_kv_block_bytes -- bytes of one block of one of K or V for one layer

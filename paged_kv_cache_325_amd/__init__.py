@@ -25,7 +25,8 @@ __all__ = [
     "PKV_FP32", "PKV_BF16", "PkvError", "lib_path", "load_library",
     "pkv_kv_store", "pkv_paged_decode", "pkv_paged_decode_partials", "pkv_paged_decode_merge",
     "pkv_paged_decode_workspace_bytes",
-    "pkv_paged_decode_split_tokens", "pkv_paged_prefill_varlen", "pkv_kv_block_bytes",
+    "pkv_paged_decode_split_tokens", "pkv_paged_prefill_varlen",
+    "pkv_paged_prefill_workspace_bytes", "pkv_kv_block_bytes",
     "pkv_last_error",
 ]
 
@@ -74,7 +75,9 @@ def load_library() -> ctypes.CDLL:
     lib.pkv_paged_prefill_varlen.restype = c_i32
     lib.pkv_paged_prefill_varlen.argtypes = [c_i32, c_p, c_i64, c_p, c_p, c_p, c_i32, c_p, c_i32,
                                              c_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
-                                             c_i64, c_f, c_i32, c_p, c_p]
+                                             c_i64, c_f, c_i32, c_p, c_p, ctypes.c_size_t, c_p]
+    lib.pkv_paged_prefill_workspace_bytes.restype = ctypes.c_size_t
+    lib.pkv_paged_prefill_workspace_bytes.argtypes = []
     lib.pkv_kv_block_bytes.restype = c_i64
     lib.pkv_kv_block_bytes.argtypes = [c_i32, c_i32, c_i32, c_i32]
     lib.pkv_last_error.restype = ctypes.c_char_p
@@ -259,8 +262,14 @@ def pkv_paged_prefill_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: to
                              context_lens: torch.Tensor, max_context_len: int,
                              block_tables: torch.Tensor, scale: float,
                              out: Optional[torch.Tensor] = None, causal: int = 1,
+                             workspace: Optional[torch.Tensor] = None,
                              stream=None) -> torch.Tensor:
-    """Varlen causal prefill: q [total_q, Hq, D] bf16 -> out [total_q, Hq, D]."""
+    """Varlen causal prefill: q [total_q, Hq, D] bf16 -> out [total_q, Hq, D].
+
+    ``workspace`` holds the kernel's work-queue counters: zero-filled before
+    its first use, left zero by every call.  Without one, a zero-filled
+    workspace kept per (device, stream) is used, so calls on one stream never
+    share counters with calls running concurrently on another."""
     lib = load_library()
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _gpu(t, n)
@@ -282,9 +291,32 @@ def pkv_paged_prefill_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: to
     _gpu(out, "out")
     if out.shape != (total, hq, d) or not out.is_contiguous() or out.dtype != q.dtype:
         raise ValueError("out must be a contiguous [total_q, Hq, D] tensor of q's dtype")
+    st = _stream(stream)
+    if workspace is None:
+        workspace = _prefill_workspace(q.device, st)
+    _gpu(workspace, "workspace")
+    ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib.pkv_paged_prefill_varlen(_dtype_code(q), _ptr(q), qs, _ptr(k_cache), _ptr(v_cache),
                                         _ptr(cu_seqlens_q), int(max_seqlen_q), _ptr(context_lens),
                                         int(max_context_len), _ptr(block_tables),
                                         int(block_tables.shape[1]), batch, hq, hkv, d, bs, nblk,
-                                        float(scale), int(causal), _ptr(out), _stream(stream)))
+                                        float(scale), int(causal), _ptr(out), _ptr(workspace),
+                                        ws_bytes, st))
     return out
+
+
+_PREFILL_WS = {}
+
+
+def pkv_paged_prefill_workspace_bytes() -> int:
+    return int(load_library().pkv_paged_prefill_workspace_bytes())
+
+
+def _prefill_workspace(device, stream_handle) -> torch.Tensor:
+    key = (device.index, stream_handle)
+    ws = _PREFILL_WS.get(key)
+    if ws is None:
+        n = (pkv_paged_prefill_workspace_bytes() + 3) // 4
+        ws = torch.zeros(n, dtype=torch.int32, device=device)
+        _PREFILL_WS[key] = ws
+    return ws

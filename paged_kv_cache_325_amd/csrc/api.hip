@@ -279,7 +279,8 @@ pkv_status pkv_paged_prefill_varlen(pkv_dtype dtype, const void* q, int64_t q_to
                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
                                     int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                     int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                                    float scale, int32_t causal, void* out, void* stream) {
+                                    float scale, int32_t causal, void* out, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
   const int eb = elem_bytes(dtype);
   if (eb == 0) return fail(PKV_ERR_INVALID, "unknown dtype %d", (int)dtype);
   if (batch < 0 || max_seqlen_q < 0 || max_context_len < 0 || max_blocks_per_seq < 0 ||
@@ -310,6 +311,10 @@ pkv_status pkv_paged_prefill_varlen(pkv_dtype dtype, const void* q, int64_t q_to
       PKV_OK)
     return st;
   if (!(scale == scale)) return fail(PKV_ERR_INVALID, "scale is NaN");
+  if (!workspace || ((uintptr_t)workspace & 3) != 0 ||
+      workspace_bytes < pkv::prefill_workspace_bytes())
+    return fail(PKV_ERR_WORKSPACE, "prefill workspace must be non-null, 4-byte aligned and >= %zu bytes",
+                pkv::prefill_workspace_bytes());
   pkv::PrefillLaunch l;
   l.q = q;
   l.q_stride = q_token_stride;
@@ -325,7 +330,10 @@ pkv_status pkv_paged_prefill_varlen(pkv_dtype dtype, const void* q, int64_t q_to
   l.num_kv_heads = num_kv_heads;
   l.scale = scale;
   l.out = out;
+  l.workspace = workspace;
   return hip_status(pkv::launch_prefill(l, (hipStream_t)stream), "paged_prefill_varlen launch");
 }
+
+size_t pkv_paged_prefill_workspace_bytes(void) { return pkv::prefill_workspace_bytes(); }
 
 }  // extern "C"

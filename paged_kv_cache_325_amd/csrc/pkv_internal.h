@@ -71,8 +71,10 @@ struct PrefillLaunch {
   int32_t batch, num_q_heads, num_kv_heads;
   float scale;
   void* out;
+  void* workspace;  // prefill_workspace_bytes(), zero on entry, zero on exit
 };
 
+size_t prefill_workspace_bytes();
 hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream);
 
 }  // namespace pkv

@@ -41,6 +41,9 @@
 // bf16 probabilities.
 #include <math.h>
 
+#include <algorithm>
+#include <atomic>
+
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -51,6 +54,7 @@ namespace {
 constexpr int kQT = 32;  // query rows per wave
 constexpr int kKT = 64;                  // keys per tile
 constexpr int kThreads = 256;
+constexpr int kMaxQueues = 8;  // one per XCD
 
 struct PrefillArgs {
   const uint16_t* q;
@@ -65,6 +69,9 @@ struct PrefillArgs {
   int32_t heads_per_wg, pos_tiles, head_chunks, max_wg_tiles;
   float scale_log2;
   uint16_t* out;
+  int32_t num_items;   // work items: (query tile, sequence, kv head, head chunk)
+  int32_t num_queues;  // work queues (one per XCD when the grid allows)
+  int32_t* counters;   // [kMaxQueues] queue heads, then the exit count
 };
 
 // Bound on the probabilities computed against a lagging running max (see
@@ -120,19 +127,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, kKT * kHeadDim * 2, 0x00020000);
 }
 
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
-  // Double-buffered K and V tiles (two named buffers, so the compiler can
-  // tell the tile being read from the tile being copied in).  64 KiB.
-  __shared__ u32x4 k_lds0[kKT * 16], k_lds1[kKT * 16];
-  __shared__ u32x4 v_lds0[kKT * 16], v_lds1[kKT * 16];
-
+// One work item: query tile r (counted from the end) of sequence b, kv
+// head g, head chunk hc; all 4 waves of the workgroup take part.  Returns
+// with every wave past the last barrier, so the LDS tiles are free again.
+__device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4* k_lds0,
+                                             u32x4* k_lds1, u32x4* v_lds0, u32x4* v_lds1) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int j = lane & 31;  // query column / MFMA row index
   const int hf = lane >> 5;
 
-  int id = blockIdx.x;
   const int hc = id % a.head_chunks;
   id /= a.head_chunks;
   const int g = id % a.num_kv_heads;
@@ -210,15 +215,22 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     // ---- S^T = K Q^T for 2 x 32 keys ------------------------------------
     f32x16 s_acc[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int key = kt * 32 + j;
+    for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb) {
+      for (int kt = 0; kt < 2; ++kt) {
+        const int key = kt * 32 + j;
         const u32x4 av = kbuf[key * 16 + k_pos(key, kb * 2 + hf)];
         s_acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             as_bf16x8(av), as_bf16x8(qreg[kb]), kb == 0 ? f32x16{} : s_acc[kt], 0, 0, 0);
       }
+    // keep 4 operand reads in flight ahead of the MFMA that consumes them
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 
     // ---- online softmax (base 2) ------------------------------------------
     // element e = rr*4 + ee of s_acc[kt] is key k0 + kt*32 + 8*rr + 4*hf + ee
@@ -302,6 +314,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
               as_bf16x8(av), as_bf16x8(pfrag[kt * 2 + ks]), o_acc[db], 0, 0, 0);
         }
     }
+    // operand reads run three MFMAs ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 1);
+#pragma unroll
+    for (int i = 0; i < 13; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 3, 1);
   };
 
   // V rows past the context (only in the last tile) are zeroed in LDS once
@@ -351,9 +371,66 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     }
 }
 
+// Persistent kernel: a grid of (at most) two workgroups per CU pulls work
+// items from num_queues atomic queues, longest item first.  Queue x holds
+// items x, x + num_queues, ...; workgroup w serves queue w % num_queues, so
+// with the round-robin placement of workgroups on the 8 XCDs every item of
+// one (sequence, kv head) runs on one XCD and shares its L2.  Dynamic
+// pulling keeps every workgroup slot busy however unequal the items are
+// (the hardware dispatcher leaves slots idle when workgroup lengths vary).
+// The last workgroup to leave resets the counters, so the workspace is zero
+// again when the kernel ends.
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
+  // Double-buffered K and V tiles (two named buffers, so the compiler can
+  // tell the tile being read from the tile being copied in).  64 KiB.
+  __shared__ u32x4 k_lds0[kKT * 16], k_lds1[kKT * 16];
+  __shared__ u32x4 v_lds0[kKT * 16], v_lds1[kKT * 16];
+  __shared__ int next_item[2];
+
+  const int queue = blockIdx.x % a.num_queues;
+  for (int it = 0;; ++it) {
+    // Alternating slots: thread 0 cannot rewrite a slot before every thread
+    // has passed the next barrier, i.e. has read it.
+    if (threadIdx.x == 0)
+      next_item[it & 1] = queue + atomicAdd(&a.counters[queue], 1) * a.num_queues;
+    __syncthreads();
+    const int id = next_item[it & 1];
+    if (id >= a.num_items) break;  // uniform over the workgroup
+    prefill_item(a, id, k_lds0, k_lds1, v_lds0, v_lds1);
+  }
+  if (threadIdx.x == 0) {
+    // acq_rel: this workgroup's queue increments are ordered before its exit
+    // count, so the last one out sees every increment and may clear them.
+    const int done = __hip_atomic_fetch_add(&a.counters[kMaxQueues], 1, __ATOMIC_ACQ_REL,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    if (done == (int)gridDim.x - 1) {
+      for (int q = 0; q <= kMaxQueues; ++q)
+        __hip_atomic_store(&a.counters[q], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 }  // namespace
 
 bool prefill_supported_group(int group) { return group == 1 || group == 2 || group % 4 == 0; }
+
+// CUs of the current device, cached per device (the grid of the persistent
+// kernel is two workgroups per CU).
+static hipError_t compute_units(int* cus) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) { *cus = c; return hipSuccess; }
+  }
+  e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (*cus <= 0) return hipErrorInvalidDevice;
+  if (dev >= 0 && dev < 64) cache[dev].store(*cus, std::memory_order_relaxed);
+  return hipSuccess;
+}
 
 hipError_t launch_prefill(const PrefillLaunch& l, hipStream_t stream) {
   PrefillArgs a;
@@ -376,11 +453,20 @@ hipError_t launch_prefill(const PrefillLaunch& l, hipStream_t stream) {
   a.max_wg_tiles = (l.max_seqlen_q + wg_rows - 1) / wg_rows;
   a.scale_log2 = l.scale * kLog2e;
   a.out = (uint16_t*)l.out;
-  const int64_t grid = (int64_t)a.max_wg_tiles * l.batch * l.num_kv_heads * a.head_chunks;
-  if (grid <= 0) return hipSuccess;
-  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const int64_t items = (int64_t)a.max_wg_tiles * l.batch * l.num_kv_heads * a.head_chunks;
+  if (items <= 0) return hipSuccess;
+  if (items > (1 << 30)) return hipErrorInvalidConfiguration;
+  int cus = 0;
+  hipError_t e = compute_units(&cus);
+  if (e != hipSuccess) return e;
+  const int grid = (int)std::min<int64_t>(items, 2 * (int64_t)cus);
+  a.num_items = (int32_t)items;
+  a.num_queues = std::min(grid, kMaxQueues);
+  a.counters = (int32_t*)l.workspace;
   hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
+
+size_t prefill_workspace_bytes() { return (kMaxQueues + 1) * sizeof(int32_t); }
 
 }  // namespace pkv

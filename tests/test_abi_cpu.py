@@ -123,13 +123,13 @@ def test_decode_split_plan():
 def _prefill(**kw):
     a = dict(dtype=BF16, q=FAKE, qs=32 * 128, kc=FAKE, vc=FAKE, cu=FAKE, maxq=100, ctx=FAKE,
              maxctx=612, bt=FAKE, mb=4, batch=2, hq=32, hkv=8, d=128, bs=256, nblk=8,
-             scale=0.088, causal=1, out=FAKE)
+             scale=0.088, causal=1, out=FAKE, ws=FAKE, wsb=64)
     a.update(kw)
     lib = pkv.load_library()
     return lib.pkv_paged_prefill_varlen(a["dtype"], a["q"], a["qs"], a["kc"], a["vc"], a["cu"],
                                         a["maxq"], a["ctx"], a["maxctx"], a["bt"], a["mb"],
                                         a["batch"], a["hq"], a["hkv"], a["d"], a["bs"], a["nblk"],
-                                        a["scale"], a["causal"], a["out"], None)
+                                        a["scale"], a["causal"], a["out"], a["ws"], a["wsb"], None)
 
 
 def test_prefill_errors():
@@ -144,6 +144,17 @@ def test_prefill_errors():
     assert _prefill(q=FAKE + 4) == INVALID
     assert _prefill(batch=-3) == INVALID
     assert "causal" in (_prefill(causal=2) and pkv.pkv_last_error())
+
+
+def test_prefill_workspace():
+    need = pkv.pkv_paged_prefill_workspace_bytes()
+    assert 4 <= need <= 256 and need % 4 == 0
+    assert _prefill(ws=None) == WORKSPACE
+    assert _prefill(ws=FAKE + 2) == WORKSPACE
+    assert _prefill(wsb=need - 4) == WORKSPACE
+    assert "workspace" in pkv.pkv_last_error()
+    # an empty problem needs no workspace
+    assert _prefill(batch=0, ws=None, wsb=0) == OK
 
 
 def test_binding_refuses_cpu_tensors():

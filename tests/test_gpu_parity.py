@@ -259,6 +259,35 @@ def test_prefill_single_query_matches_decode():
     assert_close(outp.double().cpu().numpy(), expected(wp), "prefill vs oracle")
 
 
+@pytest.mark.parametrize("spec", [
+    Spec("pre-tiny-1item", "prefill", "bf16", 4, 1, [40], [40], 801),
+    Spec("pre-tiny-6items", "prefill", "bf16", 4, 1, [70, 20], [70, 20], 802),
+    Spec("pre-g4-42items", "prefill", "bf16", 8, 2, [100, 300, 7], [100, 200, 7], 803),
+], ids=lambda s: s.name)
+def test_prefill_workspace_reset_and_small_grids(spec):
+    """The persistent prefill kernel's work-queue counters: an explicit
+    workspace is zero again after every call, repeated calls are bitwise
+    identical, and grids with fewer work items than queues are complete."""
+    w = build(spec)
+    d = to_device(w)
+    check_inputs(d)
+    store(d)
+    ws = torch.zeros(pkv.pkv_paged_prefill_workspace_bytes() // 4, dtype=torch.int32,
+                     device="cuda")
+    outs = []
+    for i in range(3):
+        announce(f"{spec.name}: prefill call {i} with an explicit workspace")
+        outs.append(pkv.pkv_paged_prefill_varlen(d.q, d.k_cache, d.v_cache, d.cu_seqlens_q,
+                                                 w.max_seqlen_q, d.context_lens,
+                                                 w.max_context_len, d.block_tables, w.scale,
+                                                 workspace=ws))
+        torch.cuda.synchronize()
+        assert int(ws.abs().sum()) == 0, "workspace not reset"
+    for o in outs[1:]:
+        assert torch.equal(outs[0], o)
+    assert_close(outs[0].double().cpu().numpy(), expected(w), spec.name)
+
+
 # ---------------------------------------------------------------------------
 # the five full-size workloads
 # ---------------------------------------------------------------------------
