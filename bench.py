@@ -1,6 +1,6 @@
 """Benchmark of the paged KV-cache hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle S] [--workload 2]
                     [--no-extra] [--no-cpu] [--copy-calibration]
 
 One step = the whole per-layer hot path over one batch of the workload:
@@ -10,7 +10,9 @@ already resident in HBM.  Before every step (warm-up and timed) a 1 GiB buffer
 is *read* (a row-wise max) to evict the 256 MB MALL, so every step reads the
 KV cache from HBM.  The eviction reads rather than writes: a write would leave
 up to 256 MB of dirty lines whose write-back would then be charged to the
-measured step.  The step itself is timed with HIP events recorded on the
+measured step.  Before the warm-up steps the step runs back to back for
+``--settle`` seconds (default 1) so that the GPU has left its idle clocks.
+The step itself is timed with HIP events recorded on the
 stream the kernels run on, which excludes the eviction.  The timed region (K steps) is
 bracketed by device synchronisation.
 
@@ -139,12 +141,24 @@ def make_flush(torch):
     return lambda: torch.amax(buf, dim=1)
 
 
-def time_steps(d: Device, steps: int, warmup: int, torch):
+def time_steps(d: Device, steps: int, warmup: int, torch, settle_s: float = 0.0):
     """Per-step event times in ms, MALL evicted before each step: the store,
-    then each attention launch (decode: partials, merge; prefill: one)."""
+    then each attention launch (decode: partials, merge; prefill: one).
+
+    Before the warm-up steps the step runs back to back for ``settle_s``
+    seconds: an idle GPU takes a while to reach its steady clocks, and a few
+    warm-up steps do not cover that ramp."""
     flush = make_flush(torch)
     stream = torch.cuda.current_stream()
     parts = d.attend_parts()
+    t_end = time.perf_counter() + settle_s
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            flush()
+            d.store()
+            for p in parts:
+                p()
+        torch.cuda.synchronize()
     for i in range(warmup):
         flush()
         d.store()
@@ -194,7 +208,7 @@ def traffic_for(kernel: str, workload: str):
     return rec["bytes"]
 
 
-def measure(index: int, steps: int, warmup: int, torch):
+def measure(index: int, steps: int, warmup: int, torch, settle_s: float):
     from workloads import config
 
     t = time.perf_counter()
@@ -202,7 +216,7 @@ def measure(index: int, steps: int, warmup: int, torch):
     log(f"workload {index} ({w.spec.name}) generated in {time.perf_counter() - t:.1f}s")
     d = Device(w, torch)
     d.check()
-    store_ms, part_ms, wall = time_steps(d, steps, warmup, torch)
+    store_ms, part_ms, wall = time_steps(d, steps, warmup, torch, settle_s)
     attn_ms = [sum(x) for x in zip(*part_ms)]
     step_ms = [a + b for a, b in zip(store_ms, attn_ms)]
     r = {
@@ -290,6 +304,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle", type=float, default=1.0,
+                    help="seconds of back-to-back untimed steps before the warm-up steps, "
+                         "so the GPU reaches its steady clocks")
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -315,7 +332,7 @@ def main() -> int:
     if args.copy_calibration:
         copy_calibration(torch)
 
-    head = measure(args.workload, args.steps, args.warmup, torch)
+    head = measure(args.workload, args.steps, args.warmup, torch, args.settle)
     w = head["w"]
     log(f"headline: step {head['step_ms']:.4f} ms, decode {head['attn_ms']:.4f} ms, "
         f"store {head['store_ms']:.4f} ms")
@@ -325,7 +342,8 @@ def main() -> int:
         for idx in (1, 2, 3, 4, 5):
             if idx == args.workload:
                 continue
-            r = measure(idx, max(3, args.steps // 2), max(1, args.warmup // 2), torch)
+            r = measure(idx, max(3, args.steps // 2), max(1, args.warmup // 2), torch,
+                        args.settle / 2)
             e = {"step_ms": round(r["step_ms"], 4), "store_ms": round(r["store_ms"], 4),
                  "attn_ms": round(r["attn_ms"], 4)}
             if "tflops" in r:
@@ -390,7 +408,8 @@ def main() -> int:
         "hbm_frac": round(head.get("attn_gbs", 0.0) / HBM_PEAK_GBS, 4),
         "store_ms": round(head["store_ms"], 5),
         "timing": "HIP events on the kernels' stream, mean over the timed steps; 1 GiB "
-                  "read-only MALL eviction before every step (outside the events)",
+                  "read-only MALL eviction before every step (outside the events); "
+                  f"{args.settle:g} s of untimed back-to-back steps before the warm-up",
         "wall_s_timed_region": round(head["wall_s"], 3),
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -6,7 +6,7 @@
 
 #include <string>
 
-#include "../../include/pkv.h"
+#include "pkv.h"
 #include "pkv_internal.h"
 
 namespace {

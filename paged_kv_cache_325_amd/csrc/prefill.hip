@@ -373,13 +373,14 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4
 
 // Persistent kernel: a grid of (at most) two workgroups per CU pulls work
 // items from num_queues atomic queues, longest item first.  Queue x holds
-// items x, x + num_queues, ...; workgroup w serves queue w % num_queues, so
-// with the round-robin placement of workgroups on the 8 XCDs every item of
-// one (sequence, kv head) runs on one XCD and shares its L2.  Dynamic
-// pulling keeps every workgroup slot busy however unequal the items are
-// (the hardware dispatcher leaves slots idle when workgroup lengths vary).
-// The last workgroup to leave resets the counters, so the workspace is zero
-// again when the kernel ends.
+// items x, x + num_queues, ...; workgroup w starts on queue w % num_queues,
+// so with the round-robin placement of workgroups on the 8 XCDs the items of
+// one (sequence, kv head) run on one XCD and share its L2.  A workgroup whose
+// queue is exhausted moves on to the next queue, so no XCD idles while
+// another still has items.  Dynamic pulling keeps every workgroup slot busy
+// however unequal the items are (the hardware dispatcher leaves slots idle
+// when workgroup lengths vary).  The last workgroup to leave resets the
+// counters, so the workspace is zero again when the kernel ends.
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   // Double-buffered K and V tiles (two named buffers, so the compiler can
   // tell the tile being read from the tile being copied in).  64 KiB.
@@ -387,16 +388,33 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   __shared__ u32x4 v_lds0[kKT * 16], v_lds1[kKT * 16];
   __shared__ int next_item[2];
 
-  const int queue = blockIdx.x % a.num_queues;
+  const int nq = a.num_queues;
+  // queue state, used by thread 0 only
+  int queue = blockIdx.x % nq;
+  int exhausted = 0;  // queues found empty so far
+  // blocking pull: the next item, or -1 once every queue is exhausted
+  auto pull = [&]() -> int {
+    while (exhausted < nq) {
+      const int id = queue + atomicAdd(&a.counters[queue], 1) * nq;
+      if (id < a.num_items) return id;
+      queue = queue + 1 == nq ? 0 : queue + 1;
+      ++exhausted;
+    }
+    return -1;
+  };
+
+  if (threadIdx.x == 0) next_item[0] = pull();
+  __syncthreads();
   for (int it = 0;; ++it) {
-    // Alternating slots: thread 0 cannot rewrite a slot before every thread
-    // has passed the next barrier, i.e. has read it.
-    if (threadIdx.x == 0)
-      next_item[it & 1] = queue + atomicAdd(&a.counters[queue], 1) * a.num_queues;
-    __syncthreads();
-    const int id = next_item[it & 1];
-    if (id >= a.num_items) break;  // uniform over the workgroup
+    // uniform over the workgroup; readfirstlane lets the compiler keep the
+    // item's indices (and the block-table entries) in scalar registers
+    const int id = __builtin_amdgcn_readfirstlane(next_item[it & 1]);
+    if (id < 0) break;
     prefill_item(a, id, k_lds0, k_lds1, v_lds0, v_lds1);
+    // Alternating slots: thread 0 cannot rewrite a slot before every thread
+    // has passed the barrier below, i.e. has read it.
+    if (threadIdx.x == 0) next_item[(it + 1) & 1] = pull();
+    __syncthreads();
   }
   if (threadIdx.x == 0) {
     // acq_rel: this workgroup's queue increments are ordered before its exit
