@@ -17,21 +17,24 @@
 // O^T += V^T * P^T; the V^T operand is read straight from the natural V tile
 // with the LDS transpose read (ds_read_b64_tr_b16).
 //
-// Work decomposition.  A workgroup is 4 wavefronts and owns one kv head g of
-// one sequence and 4 "query tiles" of 32 rows: 4 query heads of g's group
-// at the same 32 positions (group >= 4), or 2 heads x 64 positions (group 2),
-// or 1 head x 128 positions (group 1).  The 4 waves share every K/V tile the
-// workgroup stages, so each K/V byte is fetched once per 128 query rows.
-// Keys are processed in tiles of 64 (a tile never crosses a 256-token block,
-// so one block-table lookup per tile).  Workgroups are ordered
-// last-query-tile first (most keys first), and consecutive workgroup ids
-// differ in kv head, so with 8 kv heads all tiles of one (sequence, kv head)
-// land on the same XCD and share its L2.
+// Work decomposition.  A work item is 8 wavefronts x 32 query rows of one
+// kv head g of one sequence: 4 query heads of g's group x 64 positions
+// (group >= 4), 2 heads x 128 positions (group 2) or 1 head x 256 positions
+// (group 1).  All 8 waves share every K/V tile the workgroup stages.  Keys
+// are processed in tiles of 64 (a tile never crosses a 256-token block, so
+// one block-table entry per tile; the item's entries are loaded once).
+// Items are numbered last-query-tile first (most keys first) and handed
+// out by a persistent kernel (one workgroup per CU) from per-XCD queues, so
+// the items of one (sequence, kv head) share one L2.
 //
-// Staging.  K and V tiles are copied global -> LDS with the direct-to-LDS
-// buffer load (no registers, no VALU), double-buffered: the copy of tile
-// t+1 is in flight while tile t is consumed.  64 KiB of LDS per workgroup,
-// two workgroups per CU.
+// Schedule.  The 8 waves form two groups of 4 (one wave of each group per
+// SIMD); every tile is an MFMA phase (PV of the previous tile, S of this
+// one) and a softmax phase, with group B one phase behind group A and a
+// workgroup barrier between phases.  Group A copies K and V tiles global ->
+// LDS with the direct-to-LDS buffer load (no registers, no VALU) two tiles
+// ahead into 4 rotating slots (128 KiB of LDS).  The buffer resource of a
+// copy covers only the tile's rows inside the context, so rows past it
+// arrive as zeros.
 //
 // Softmax work per tile is kept small because it competes with the MFMAs
 // for issue slots: the causal mask is a select, the scale is folded into
@@ -51,10 +54,15 @@ namespace pkv {
 
 namespace {
 
-constexpr int kQT = 32;  // query rows per wave
-constexpr int kKT = 64;                  // keys per tile
-constexpr int kThreads = 256;
-constexpr int kMaxQueues = 8;  // one per XCD
+constexpr int kQT = 32;          // query rows per wave
+constexpr int kKT = 64;          // keys per tile
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kGroupWaves = 4;   // waves per ping-pong group
+constexpr int kSlots = 4;        // LDS slots for K and for V tiles
+constexpr int kAhead = 2;        // tiles copied ahead of the phase that first reads them
+constexpr int kCopyOps = 8;      // direct-to-LDS loads per group-A wave per tile (K 4, V 4)
+constexpr int kMaxQueues = 8;    // one per XCD
 
 struct PrefillArgs {
   const uint16_t* q;
@@ -98,10 +106,10 @@ __device__ __forceinline__ int k_pos(int key, int c) { return c ^ (key & 15); }
 __device__ __forceinline__ int v_pos(int key, int c) { return c ^ ((key & 7) << 1); }
 
 // Copy one 64-key tile (K or V, rows k0 .. k0+63 of a (block, kv head),
-// `rsrc` addressing its 16 KiB) into LDS: each of the 4 waves moves 16
-// keys, 1 KiB per instruction.  The per-lane byte offsets depend only on the
-// lane and wave, so they are computed once per kernel (tile_offsets) and a
-// new tile only changes the scalar buffer base.
+// `rsrc` addressing it) into LDS: each of the 4 group-A waves moves 16 keys,
+// 1 KiB per instruction.  The per-lane byte offsets depend only on the lane
+// and wave, so they are computed once (tile_offsets) and a new tile only
+// changes the scalar buffer base.
 template <bool kIsV>
 __device__ __forceinline__ void tile_offsets(uint32_t (&voff)[4], int wave, int lane) {
 #pragma unroll
@@ -121,22 +129,44 @@ __device__ __forceinline__ void tile_to_lds(__amdgpu_buffer_rsrc_t rsrc, const u
                                              voff[i], 0, 0, 0);
 }
 
-// Raw buffer resource over one 16 KiB K or V tile (word 3: 32-bit data
-// format, the value used for untyped buffer access on gfx9-family parts).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base) {
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, kKT * kHeadDim * 2, 0x00020000);
+// Raw buffer resource over the valid rows of one K or V tile (word 3:
+// 32-bit data format, the value used for untyped buffer access on
+// gfx9-family parts).  Loads past `bytes` return zero, so the rows of a
+// tile that lie past the context arrive in LDS as zeros: masked
+// probabilities are 0 and 0 * 0 stays 0 in the PV product.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, 0x00020000);
 }
 
-// One work item: query tile r (counted from the end) of sequence b, kv
-// head g, head chunk hc; all 4 waves of the workgroup take part.  Returns
-// with every wave past the last barrier, so the LDS tiles are free again.
-__device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4* k_lds0,
-                                             u32x4* k_lds1, u32x4* v_lds0, u32x4* v_lds1) {
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8).
+template <int kVm>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(kVm >= 0 && kVm < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | kVm);
+}
+
+// Barrier between phases.  No memory fence: copies issued for later tiles
+// stay in flight (their completion is awaited explicitly with vmcnt).  This
+// wave's LDS accesses complete first, and the compiler may not move memory
+// accesses across it.
+__device__ __forceinline__ void phase_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One work item: query tile r (counted from the end) of sequence b, kv head
+// g, head chunk hc, on 8 waves in two groups of 4 (see the kernel).
+__device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4 (*kbuf)[kKT * 16],
+                                             u32x4 (*vbuf)[kKT * 16]) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int j = lane & 31;  // query column / MFMA row index
   const int hf = lane >> 5;
+  const bool group_a = wave < kGroupWaves;
 
   const int hc = id % a.head_chunks;
   id /= a.head_chunks;
@@ -151,7 +181,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4
   const int off = n_k - n_q;
   const int wg_rows = kQT * a.pos_tiles;
   const int wg_tiles = (n_q + wg_rows - 1) / wg_rows;
-  if (r >= wg_tiles) return;  // uniform over the workgroup
+  if (r >= wg_tiles) return;  // uniform over the workgroup, before any barrier
   const int wg_q0 = (wg_tiles - 1 - r) * wg_rows;
 
   const int my_q0 = wg_q0 + (wave / a.heads_per_wg) * kQT;
@@ -159,8 +189,9 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4
   const bool wave_has_rows = my_q0 < n_q;
   // keys seen by the last query of the workgroup / of this wave
   const int wg_kend = max(0, min(n_k, off + min(n_q, wg_q0 + wg_rows)));
-  const int my_kend = max(0, min(n_k, off + min(n_q, my_q0 + kQT)));
+  const int my_kend = wave_has_rows ? max(0, min(n_k, off + min(n_q, my_q0 + kQT))) : 0;
   const int ntiles = (wg_kend + kKT - 1) / kKT;
+  const int my_tiles = (my_kend + kKT - 1) / kKT;
 
   // this lane's query column: row qi of the sequence (clamped for loads)
   const int qi = my_q0 + j;
@@ -180,16 +211,31 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4
   float l_part = 0.f;
   const float c = a.scale_log2;
 
+  // Block-table entries of the item, loaded once: lane i holds logical
+  // blocks i and 64 + i; beyond 128 blocks a scalar load (constant address
+  // space) is used.  A per-tile global load would make the copy wait on
+  // every vector memory access in flight, including the copies of the
+  // previous tiles.
   const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
+  const int nblk = (wg_kend + kBlockSize - 1) / kBlockSize;
+  const int32_t tab0 = lane < nblk ? table[lane] : 0;
+  const int32_t tab1 = lane + 64 < nblk ? table[lane + 64] : 0;
+  auto block_at = [&](int i) -> int64_t {  // i uniform
+    if (i < 64) return __builtin_amdgcn_readlane(tab0, i);
+    if (i < 128) return __builtin_amdgcn_readlane(tab1, i - 64);
+    return ((const __attribute__((address_space(4))) int32_t*)table)[i];
+  };
   uint32_t k_off[4], v_off[4];
-  tile_offsets<false>(k_off, wave, lane);
-  tile_offsets<true>(v_off, wave, lane);
-  auto issue_copy = [&](int t, u32x4* kbuf, u32x4* vbuf) {
+  tile_offsets<false>(k_off, wave & (kGroupWaves - 1), lane);
+  tile_offsets<true>(v_off, wave & (kGroupWaves - 1), lane);
+  auto issue_copy = [&](int t) {  // group A only
     const int k0 = t * kKT;
-    const int64_t blk = table[k0 / kBlockSize];
+    const int64_t blk = block_at(k0 / kBlockSize);
     const int64_t base = ((blk * a.num_kv_heads + g) * kBlockSize + (k0 % kBlockSize)) * kHeadDim;
-    tile_to_lds(tile_rsrc(a.k_cache + base), k_off, kbuf, wave);
-    tile_to_lds(tile_rsrc(a.v_cache + base), v_off, vbuf, wave);
+    const int bytes = min(kKT, n_k - k0) * (kHeadDim * 2);
+    const int slot = t % kSlots;
+    tile_to_lds(tile_rsrc(a.k_cache + base, bytes), k_off, kbuf[slot], wave);
+    tile_to_lds(tile_rsrc(a.v_cache + base, bytes), v_off, vbuf[slot], wave);
   };
 
   // PV operand reads (ds_read_b64_tr_b16): in each 16-lane group, lane
@@ -201,38 +247,41 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4
   const int tr_g = lane >> 4;
   const int tr_a = lane & 3;
   const int tr_m = (lane >> 2) & 3;
-  auto tr_read = [&](const u32x4* vbuf, int key, int dim) -> uint64_t {
+  auto tr_read = [&](const u32x4* vb, int key, int dim) -> uint64_t {
     const int cpos = v_pos(key, dim >> 3);
-    const char* p = reinterpret_cast<const char*>(vbuf) + key * 256 + cpos * 16 + (dim & 7) * 2;
+    const char* p = reinterpret_cast<const char*>(vb) + key * 256 + cpos * 16 + (dim & 7) * 2;
     const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
     return __builtin_bit_cast(uint64_t, v);
   };
 
-  auto tile = [&](int t, const u32x4* kbuf, u32x4* vbuf) {
-    const int k0 = t * kKT;
-    if (!wave_has_rows || k0 >= my_kend) return;  // uniform over the wave
+  f32x16 s_acc[2];
+  u32x4 pfrag[4];  // B operands of the PV product: (kt, ks) -> 16 keys
 
-    // ---- S^T = K Q^T for 2 x 32 keys ------------------------------------
-    f32x16 s_acc[2];
+  // ---- S^T = K Q^T for the 64 keys of tile t --------------------------------
+  auto scores = [&](int t) {
+    const u32x4* kb_ = kbuf[t % kSlots];
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         const int key = kt * 32 + j;
-        const u32x4 av = kbuf[key * 16 + k_pos(key, kb * 2 + hf)];
+        const u32x4 av = kb_[key * 16 + k_pos(key, kb * 2 + hf)];
         s_acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             as_bf16x8(av), as_bf16x8(qreg[kb]), kb == 0 ? f32x16{} : s_acc[kt], 0, 0, 0);
       }
     // keep 4 operand reads in flight ahead of the MFMA that consumes them
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
-    for (int i = 0; i < 12; ++i) {
+    for (int i = 0; i < 10; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+  };
 
-    // ---- online softmax (base 2) ------------------------------------------
+  // ---- online softmax (base 2) of tile t -> pfrag --------------------------
+  auto softmax = [&](int t) {
+    const int k0 = t * kKT;
     // element e = rr*4 + ee of s_acc[kt] is key k0 + kt*32 + 8*rr + 4*hf + ee
     if ((k0 + kKT - 1 > off + my_q0) || (k0 + kKT > n_k)) {
       // masked keys (past the query's position or the context) -> -inf
@@ -251,7 +300,6 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4
     // reference m_run may lag the true max -- softmax is invariant to it --
     // and O, l need no rescaling.  Otherwise (or on a query's first visible
     // tile) m_run moves to the true running max and the tile is redone.
-    u32x4 pfrag[4];  // B operands: (kt, ks) -> 16 keys
     float psum;
     auto probs = [&](float neg_m) {
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -296,8 +344,11 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4
       probs(m_new == -INFINITY ? 0.f : -m_new);
     }
     l_part += psum;
+  };
 
-    // ---- O^T += V^T P^T ------------------------------------------------------
+  // ---- O^T += V^T P^T for tile t ---------------------------------------------
+  auto pv = [&](int t) {
+    const u32x4* vb = vbuf[t % kSlots];
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const int dim = db * 32 + 16 * (tr_g & 1) + 4 * tr_a;
@@ -306,8 +357,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const int key = kt * 32 + ks * 16 + 4 * hf + tr_m;
-          const uint64_t lo = tr_read(vbuf, key, dim);
-          const uint64_t hi = tr_read(vbuf, key + 8, dim);
+          const uint64_t lo = tr_read(vb, key, dim);
+          const uint64_t hi = tr_read(vb, key + 8, dim);
           const u32x4 av = u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi,
                                  (uint32_t)(hi >> 32)};
           o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -315,45 +366,51 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4
         }
     }
     // operand reads run three MFMAs ahead
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 10, 1);
 #pragma unroll
-    for (int i = 0; i < 13; ++i) {
+    for (int i = 0; i < 11; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 3, 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, 5, 1);
   };
 
-  // V rows past the context (only in the last tile) are zeroed in LDS once
-  // the tile has arrived: p = 0 there, but 0 * NaN poison inside an MFMA
-  // would still be NaN.
-  auto clear_tail = [&](int t, u32x4* vbuf) {
-    const int k0 = t * kKT;
-    if (k0 + kKT <= n_k) return;  // uniform over the workgroup
-    for (int i = tid; i < kKT * 16; i += kThreads)
-      if (k0 + i / 16 >= n_k) vbuf[i] = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();
-  };
-
-  // Tiles alternate between buffer 0 (even t) and buffer 1 (odd t).  The
-  // copy of tile t+1 is issued before tile t is consumed; the barrier at the
-  // end of each step makes tile t+1 visible and frees tile t's buffer.
-  if (ntiles > 0) issue_copy(0, k_lds0, v_lds0);
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's copies landed
-  __syncthreads();
-  for (int t = 0; t < ntiles; t += 2) {
-    if (t + 1 < ntiles) issue_copy(t + 1, k_lds1, v_lds1);
-    clear_tail(t, v_lds0);
-    tile(t, k_lds0, v_lds0);
-    __builtin_amdgcn_s_waitcnt(0x0f70);
-    __syncthreads();
-    if (t + 1 >= ntiles) break;
-    if (t + 2 < ntiles) issue_copy(t + 2, k_lds0, v_lds0);
-    clear_tail(t + 1, v_lds1);
-    tile(t + 1, k_lds1, v_lds1);
-    __builtin_amdgcn_s_waitcnt(0x0f70);
-    __syncthreads();
+  // ---- ping-pong schedule ------------------------------------------------------
+  // Each tile t is an MFMA phase M(t) = {PV(t-1), S(t)} followed by a VALU
+  // phase V(t) = softmax(t).  Group B runs one phase behind group A, and
+  // every phase ends in a workgroup barrier, so while the waves of one group
+  // issue MFMAs the waves of the other (on the same SIMDs) run the softmax.
+  // Group A copies tile t+2 during V(t) (slots rotate over 4 tiles: K(t) is
+  // last read by B in M(t), V(t) by B in M(t+1)); before the barrier that
+  // ends V(t) it waits for its copies of tile t+1.
+  if (group_a) {
+    if (ntiles > 0) issue_copy(0);
+    if (ntiles > 1) {
+      issue_copy(1);
+      wait_vmcnt<kCopyOps>();
+    } else {
+      wait_vmcnt<0>();
+    }
   }
+  phase_barrier();
+  if (!group_a) phase_barrier();  // B starts one phase behind
+  for (int t = 0; t < ntiles; ++t) {
+    if (t >= 1 && t - 1 < my_tiles) pv(t - 1);
+    if (t < my_tiles) scores(t);
+    phase_barrier();
+    if (t < my_tiles) softmax(t);
+    if (group_a) {
+      if (t + kAhead < ntiles) {
+        issue_copy(t + kAhead);
+        wait_vmcnt<kCopyOps>();
+      } else {
+        wait_vmcnt<0>();
+      }
+    }
+    phase_barrier();
+  }
+  if (ntiles >= 1 && ntiles - 1 < my_tiles) pv(ntiles - 1);
+  if (group_a) phase_barrier();  // matches B's extra barrier at the start
 
   // ---- epilogue: out[q_row][h][d] = O^T[d][j] / l ---------------------------
   if (!wave_has_rows || qi >= n_q) return;
@@ -371,21 +428,20 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4
     }
 }
 
-// Persistent kernel: a grid of (at most) two workgroups per CU pulls work
-// items from num_queues atomic queues, longest item first.  Queue x holds
-// items x, x + num_queues, ...; workgroup w starts on queue w % num_queues,
-// so with the round-robin placement of workgroups on the 8 XCDs the items of
-// one (sequence, kv head) run on one XCD and share its L2.  A workgroup whose
+// Persistent kernel: one workgroup of 8 waves per CU pulls work items from
+// num_queues atomic queues, longest item first.  Queue x holds items x,
+// x + num_queues, ...; workgroup w starts on queue w % num_queues, so with
+// the round-robin placement of workgroups on the 8 XCDs the items of one
+// (sequence, kv head) run on one XCD and share its L2.  A workgroup whose
 // queue is exhausted moves on to the next queue, so no XCD idles while
-// another still has items.  Dynamic pulling keeps every workgroup slot busy
+// another still has items.  Dynamic pulling keeps every workgroup busy
 // however unequal the items are (the hardware dispatcher leaves slots idle
 // when workgroup lengths vary).  The last workgroup to leave resets the
 // counters, so the workspace is zero again when the kernel ends.
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
-  // Double-buffered K and V tiles (two named buffers, so the compiler can
-  // tell the tile being read from the tile being copied in).  64 KiB.
-  __shared__ u32x4 k_lds0[kKT * 16], k_lds1[kKT * 16];
-  __shared__ u32x4 v_lds0[kKT * 16], v_lds1[kKT * 16];
+__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
+  // K and V tiles, 4 slots each (128 KiB).
+  __shared__ u32x4 kbuf[kSlots][kKT * 16];
+  __shared__ u32x4 vbuf[kSlots][kKT * 16];
   __shared__ int next_item[2];
 
   const int nq = a.num_queues;
@@ -404,17 +460,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   };
 
   if (threadIdx.x == 0) next_item[0] = pull();
-  __syncthreads();
+  phase_barrier();
   for (int it = 0;; ++it) {
     // uniform over the workgroup; readfirstlane lets the compiler keep the
     // item's indices (and the block-table entries) in scalar registers
     const int id = __builtin_amdgcn_readfirstlane(next_item[it & 1]);
     if (id < 0) break;
-    prefill_item(a, id, k_lds0, k_lds1, v_lds0, v_lds1);
+    prefill_item(a, id, kbuf, vbuf);
     // Alternating slots: thread 0 cannot rewrite a slot before every thread
     // has passed the barrier below, i.e. has read it.
     if (threadIdx.x == 0) next_item[(it + 1) & 1] = pull();
-    __syncthreads();
+    phase_barrier();
   }
   if (threadIdx.x == 0) {
     // acq_rel: this workgroup's queue increments are ordered before its exit
@@ -433,7 +489,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 bool prefill_supported_group(int group) { return group == 1 || group == 2 || group % 4 == 0; }
 
 // CUs of the current device, cached per device (the grid of the persistent
-// kernel is two workgroups per CU).
+// kernel is one workgroup per CU).
 static hipError_t compute_units(int* cus) {
   static std::atomic<int> cache[64];
   int dev = 0;
@@ -465,7 +521,7 @@ hipError_t launch_prefill(const PrefillLaunch& l, hipStream_t stream) {
   a.num_kv_heads = l.num_kv_heads;
   a.group = l.num_q_heads / l.num_kv_heads;
   a.heads_per_wg = a.group >= 4 ? 4 : a.group;
-  a.pos_tiles = 4 / a.heads_per_wg;
+  a.pos_tiles = kWaves / a.heads_per_wg;
   a.head_chunks = a.group / a.heads_per_wg;
   const int wg_rows = kQT * a.pos_tiles;
   a.max_wg_tiles = (l.max_seqlen_q + wg_rows - 1) / wg_rows;
@@ -477,7 +533,7 @@ hipError_t launch_prefill(const PrefillLaunch& l, hipStream_t stream) {
   int cus = 0;
   hipError_t e = compute_units(&cus);
   if (e != hipSuccess) return e;
-  const int grid = (int)std::min<int64_t>(items, 2 * (int64_t)cus);
+  const int grid = (int)std::min<int64_t>(items, (int64_t)cus);
   a.num_items = (int32_t)items;
   a.num_queues = std::min(grid, kMaxQueues);
   a.counters = (int32_t*)l.workspace;
