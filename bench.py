@@ -188,6 +188,53 @@ def mean(x):
     return sum(x) / len(x)
 
 
+def time_fused_step(d: Device, steps: int, torch):
+    """The decode step as one call (pkv_paged_decode_step: store fused into
+    the decode), eager and replayed from a captured graph; mean event-timed
+    ms per step, MALL evicted before each step as in time_steps."""
+    import paged_kv_cache_325_amd as pkv
+
+    w = d.w
+
+    def step():
+        pkv.pkv_paged_decode_step(d.q, d.k, d.v, d.slot_mapping, d.k_cache, d.v_cache,
+                                  d.block_tables, d.context_lens, w.max_context_len, w.scale,
+                                  out=d.out, workspace=d.workspace)
+
+    flush = make_flush(torch)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(3):
+            flush()
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for e0, e1 in evs:
+            flush()
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return mean([e0.elapsed_time(e1) for e0, e1 in evs])
+
+    eager_ms = timed(step)
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    graph_ms = timed(graph.replay)
+    del flush
+    return eager_ms, graph_ms
+
+
 # HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE runs (KiB per
 # dispatch, scaled by the same counters on a plain 256 MiB device copy), with
 # the sha256 of the kernel source they were taken on: once the source
@@ -236,6 +283,8 @@ def measure(index: int, steps: int, warmup: int, torch, settle_s: float):
     }
     kv = w.logical_kv_bytes()
     if w.spec.mode == "decode":
+        r["fused_step_ms"], r["fused_step_graph_ms"] = time_fused_step(d, max(5, steps // 2),
+                                                                      torch)
         attn_bytes = kv + w.qo_bytes()
         r["attn_bytes"] = attn_bytes
         r["attn_gbs"] = attn_bytes / (r["attn_ms"] * 1e-3) / 1e9
@@ -361,7 +410,9 @@ def main() -> int:
                 e.update(decode_gbs=round(r["attn_gbs"], 1),
                          hbm_frac=round(r["attn_gbs"] / HBM_PEAK_GBS, 4),
                          decode_unique_gbs=round(r["unique_gbs"], 1),
-                         decode_tokens_per_s=round(r["w"].batch / (r["attn_ms"] * 1e-3), 1))
+                         decode_tokens_per_s=round(r["w"].batch / (r["attn_ms"] * 1e-3), 1),
+                         fused_step_ms=round(r["fused_step_ms"], 4),
+                         fused_step_graph_ms=round(r["fused_step_graph_ms"], 4))
             extra[r["w"].spec.name] = e
             log(f"workload {idx}: {e}")
 
@@ -415,6 +466,9 @@ def main() -> int:
         "step_tokens_per_s": round(w.batch / (head["step_ms"] * 1e-3), 1),
         "hbm_frac": round(head.get("attn_gbs", 0.0) / HBM_PEAK_GBS, 4),
         "store_ms": round(head["store_ms"], 5),
+        "fused_step_ms": round(head["fused_step_ms"], 5) if "fused_step_ms" in head else None,
+        "fused_step_graph_ms": (round(head["fused_step_graph_ms"], 5)
+                                if "fused_step_graph_ms" in head else None),
         "timing": "HIP events on the kernels' stream, mean over the timed steps; 1 GiB "
                   "read-only MALL eviction before every step (outside the events); "
                   f"{args.settle:g} s of untimed back-to-back steps before the warm-up",

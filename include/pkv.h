@@ -194,6 +194,43 @@ pkv_status pkv_paged_decode_partials(
     int32_t block_size, int64_t num_blocks, float scale, int32_t num_splits,
     void* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * pkv_paged_decode_step -- one decode step of one layer in one call: the
+ * store of this step's K/V rows (one per sequence) fused into the paged
+ * decode (source study section 2: the attention layer writes k, v into the
+ * cache with the store kernel, then runs decode attention over the cache;
+ * architecture page "Prefill- und Decode-Vorbereitung": in decode each
+ * sequence appends one token whose slot is the last position of its last
+ * block).  It leaves the caches and out exactly (bitwise) as
+ * pkv_kv_store(k_new, v_new, slot_mapping, num_tokens = batch) followed by
+ * pkv_paged_decode(...) with the same split plan, provided the decode-step
+ * invariant holds for every row b:
+ *   slot_mapping[b] == -1 (no store; padding rows also have
+ *   context_lens[b] == 0), or slot_mapping[b] is the slot of position
+ *   context_lens[b] - 1 of sequence b, in a block that no other sequence's
+ *   context includes (the block manager never appends into a shared block).
+ * If the invariant is broken the store still happens, but the decode may
+ * read the slot before or after it is written.
+ *
+ *   k_new, v_new   device [batch][num_kv_heads][head_dim] (dtype), row b at
+ *                  b * *_token_stride elements
+ *   slot_mapping   device int32 [batch]
+ *   k_cache, v_cache  written (the stored rows) and read
+ *   everything else as for pkv_paged_decode (same workspace size).
+ * The split kernel does the store, so with a single split the whole step is
+ * one launch; capture in a HIP graph is safe (no allocation, no memset, no
+ * synchronisation).  Errors: as pkv_kv_store and pkv_paged_decode.
+ */
+pkv_status pkv_paged_decode_step(
+    pkv_dtype dtype, const void* q, int64_t q_token_stride, const void* k_new,
+    int64_t k_new_token_stride, const void* v_new, int64_t v_new_token_stride,
+    const int32_t* slot_mapping, void* k_cache, void* v_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, int32_t max_context_len, int32_t batch,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int64_t num_blocks, float scale, int32_t num_splits,
+    void* out, void* workspace, size_t workspace_bytes, void* stream);
+
 pkv_status pkv_paged_decode_merge(pkv_dtype dtype, const int32_t* context_lens,
                                   int32_t max_context_len, int32_t batch,
                                   int32_t num_q_heads, int32_t num_kv_heads,

@@ -8,7 +8,8 @@ missing or a tensor is not on the GPU, the call raises.
 
 Names follow the C ABI: ``pkv_kv_store``, ``pkv_paged_decode`` (and its two
 halves ``pkv_paged_decode_partials`` / ``pkv_paged_decode_merge``),
-``pkv_paged_decode_workspace_bytes``, ``pkv_paged_decode_split_tokens``,
+``pkv_paged_decode_step`` (store fused into decode), ``pkv_paged_decode_workspace_bytes``,
+``pkv_paged_decode_split_tokens``, ``pkv_paged_prefill_workspace_bytes``,
 ``pkv_paged_prefill_varlen``, ``pkv_kv_block_bytes``, ``pkv_last_error``.
 """
 
@@ -24,6 +25,7 @@ __all__ = [
     "PKV_OK", "PKV_ERR_INVALID", "PKV_ERR_UNSUPPORTED", "PKV_ERR_WORKSPACE", "PKV_ERR_HIP",
     "PKV_FP32", "PKV_BF16", "PkvError", "lib_path", "load_library",
     "pkv_kv_store", "pkv_paged_decode", "pkv_paged_decode_partials", "pkv_paged_decode_merge",
+    "pkv_paged_decode_step",
     "pkv_paged_decode_workspace_bytes",
     "pkv_paged_decode_split_tokens", "pkv_paged_prefill_varlen",
     "pkv_paged_prefill_workspace_bytes", "pkv_kv_block_bytes",
@@ -69,6 +71,10 @@ def load_library() -> ctypes.CDLL:
         fn.restype = c_i32
         fn.argtypes = [c_i32, c_p, c_i64, c_p, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_i32,
                        c_i32, c_i32, c_i64, c_f, c_i32, c_p, c_p, ctypes.c_size_t, c_p]
+    lib.pkv_paged_decode_step.restype = c_i32
+    lib.pkv_paged_decode_step.argtypes = [c_i32, c_p, c_i64, c_p, c_i64, c_p, c_i64, c_p, c_p, c_p,
+                                          c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                          c_i64, c_f, c_i32, c_p, c_p, ctypes.c_size_t, c_p]
     lib.pkv_paged_decode_merge.restype = c_i32
     lib.pkv_paged_decode_merge.argtypes = [c_i32, c_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                            c_i32, c_p, c_p, ctypes.c_size_t, c_p]
@@ -225,6 +231,53 @@ def pkv_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
     with torch if not given."""
     return _decode_call("pkv_paged_decode", q, k_cache, v_cache, block_tables, context_lens,
                         max_context_len, scale, out, workspace, num_splits, stream)[0]
+
+
+def pkv_paged_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                          slot_mapping: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          block_tables: torch.Tensor, context_lens: torch.Tensor,
+                          max_context_len: int, scale: float, out: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None, num_splits: int = 0,
+                          stream=None) -> torch.Tensor:
+    """One decode step: store k_new/v_new ([batch, Hkv, D]) at slot_mapping
+    and decode q ([batch, Hq, D]) over the cache, in one call (see
+    pkv_paged_decode_step in include/pkv.h for the decode-step invariant)."""
+    lib = load_library()
+    for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"),
+                 (v_cache, "v_cache")):
+        _gpu(t, n)
+    for t, n in ((slot_mapping, "slot_mapping"), (block_tables, "block_tables"),
+                 (context_lens, "context_lens")):
+        _int32(t, n)
+    nblk, hkv, bs, d = _cache_dims(k_cache, v_cache)
+    if q.dtype != k_cache.dtype or k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
+        raise ValueError("q, k_new, v_new and caches must share a dtype")
+    if q.dim() != 3:
+        raise ValueError("q must be [batch, num_q_heads, head_dim]")
+    batch, hq = int(q.shape[0]), int(q.shape[1])
+    qs = _rows(q, "q", hq, d)
+    ks = _rows(k_new, "k_new", hkv, d)
+    vs = _rows(v_new, "v_new", hkv, d)
+    if (k_new.shape[0] != batch or v_new.shape[0] != batch or slot_mapping.numel() != batch
+            or context_lens.numel() != batch or block_tables.dim() != 2
+            or block_tables.shape[0] != batch):
+        raise ValueError("q, k_new, v_new, slot_mapping, context_lens and block_tables must "
+                         "agree on the batch")
+    if out is None:
+        out = torch.empty((batch, hq, d), dtype=q.dtype, device=q.device)
+    _gpu(out, "out")
+    if out.shape != (batch, hq, d) or not out.is_contiguous() or out.dtype != q.dtype:
+        raise ValueError("out must be a contiguous [batch, Hq, D] tensor of q's dtype")
+    need = pkv_paged_decode_workspace_bytes(batch, hq, hkv, d, max_context_len, bs, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.pkv_paged_decode_step(
+        _dtype_code(q), _ptr(q), qs, _ptr(k_new), ks, _ptr(v_new), vs, _ptr(slot_mapping),
+        _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), int(block_tables.shape[1]),
+        _ptr(context_lens), int(max_context_len), batch, hq, hkv, d, bs, nblk, float(scale),
+        int(num_splits), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
 
 
 def pkv_paged_decode_partials(q, k_cache, v_cache, block_tables, context_lens, max_context_len,

@@ -138,6 +138,15 @@ namespace {
 
 enum DecodeParts { kSplitOnly = 1, kMergeOnly = 2, kSplitAndMerge = 3 };
 
+// This step's K/V rows for the fused store of pkv_paged_decode_step.
+struct FusedStore {
+  const void* k_new;
+  int64_t k_stride;
+  const void* v_new;
+  int64_t v_stride;
+  const int32_t* slot_mapping;
+};
+
 // Checks for the merge (and shared by the split) entry points.
 pkv_status check_decode_common(pkv_dtype dtype, int32_t batch, int32_t num_q_heads,
                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
@@ -174,7 +183,8 @@ pkv_status decode_parts(int parts, pkv_dtype dtype, const void* q, int64_t q_tok
                         int32_t max_context_len, int32_t batch, int32_t num_q_heads,
                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                         int64_t num_blocks, float scale, int32_t num_splits, void* out,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+                        void* workspace, size_t workspace_bytes, void* stream,
+                        const FusedStore* fs = nullptr) {
   const int eb = elem_bytes(dtype);
   if (eb == 0) return fail(PKV_ERR_INVALID, "unknown dtype %d", (int)dtype);
   pkv_status st = check_geometry(num_q_heads, num_kv_heads, head_dim, block_size);
@@ -204,6 +214,19 @@ pkv_status decode_parts(int parts, pkv_dtype dtype, const void* q, int64_t q_tok
       return st;
     if (!(scale == scale)) return fail(PKV_ERR_INVALID, "scale is NaN");
   }
+  if (fs) {
+    if (!fs->k_new || !fs->v_new || !fs->slot_mapping || !k_cache || !v_cache)
+      return fail(PKV_ERR_INVALID, "null k_new, v_new, slot_mapping or cache with batch = %d",
+                  batch);
+    if (num_blocks == 0) return fail(PKV_ERR_INVALID, "num_blocks is 0 but rows are to be stored");
+    if (!aligned16(fs->k_new) || !aligned16(fs->v_new))
+      return fail(PKV_ERR_INVALID, "k_new and v_new must be 16-byte aligned");
+    const int64_t row = (int64_t)num_kv_heads * head_dim;
+    if ((st = check_stride("k_new_token_stride", fs->k_stride, row, eb)) != PKV_OK) return st;
+    if ((st = check_stride("v_new_token_stride", fs->v_stride, row, eb)) != PKV_OK) return st;
+    if (num_blocks * block_size > (int64_t)INT32_MAX + 1)
+      return fail(PKV_ERR_UNSUPPORTED, "num_blocks * block_size exceeds the int32 slot range");
+  }
   pkv::DecodeLaunch l;
   l.q = q;
   l.q_stride = q_token_stride;
@@ -218,6 +241,13 @@ pkv_status decode_parts(int parts, pkv_dtype dtype, const void* q, int64_t q_tok
   l.scale = scale;
   l.out = out;
   l.workspace = plan.workspace_bytes ? (float*)workspace : nullptr;
+  if (fs) {
+    l.k_new = fs->k_new;
+    l.k_new_stride = fs->k_stride;
+    l.v_new = fs->v_new;
+    l.v_new_stride = fs->v_stride;
+    l.slot_mapping = fs->slot_mapping;
+  }
   if (parts & kSplitOnly) {
     st = hip_status(pkv::launch_decode_split(eb, plan, l, (hipStream_t)stream),
                     "paged_decode split launch");
@@ -245,6 +275,22 @@ pkv_status pkv_paged_decode(pkv_dtype dtype, const void* q, int64_t q_token_stri
                       max_blocks_per_seq, context_lens, max_context_len, batch, num_q_heads,
                       num_kv_heads, head_dim, block_size, num_blocks, scale, num_splits, out,
                       workspace, workspace_bytes, stream);
+}
+
+pkv_status pkv_paged_decode_step(pkv_dtype dtype, const void* q, int64_t q_token_stride,
+                                 const void* k_new, int64_t k_new_token_stride, const void* v_new,
+                                 int64_t v_new_token_stride, const int32_t* slot_mapping,
+                                 void* k_cache, void* v_cache, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 int32_t max_context_len, int32_t batch, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int64_t num_blocks, float scale, int32_t num_splits, void* out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  const FusedStore fs{k_new, k_new_token_stride, v_new, v_new_token_stride, slot_mapping};
+  return decode_parts(kSplitAndMerge, dtype, q, q_token_stride, k_cache, v_cache, block_tables,
+                      max_blocks_per_seq, context_lens, max_context_len, batch, num_q_heads,
+                      num_kv_heads, head_dim, block_size, num_blocks, scale, num_splits, out,
+                      workspace, workspace_bytes, stream, &fs);
 }
 
 pkv_status pkv_paged_decode_partials(pkv_dtype dtype, const void* q, int64_t q_token_stride,

@@ -76,6 +76,14 @@ struct DecodeArgs {
   uint8_t* out;
   float* ws_acc;
   float* ws_ml;
+  // Fused store (decode step): this step's K/V row of every sequence, stored
+  // at slot_mapping[b] by the kernel itself; k_new == nullptr: no store.
+  const uint8_t* k_new;
+  const uint8_t* v_new;
+  int64_t k_new_stride_bytes, v_new_stride_bytes;
+  const int32_t* slot_mapping;
+  uint8_t* k_cache_w;
+  uint8_t* v_cache_w;
 };
 
 struct TrueTag { static constexpr bool value = true; };
@@ -95,7 +103,7 @@ __device__ __forceinline__ void unpack(const u32x4& w, float* f) {
   }
 }
 
-template <int kElemBytes, int kHeads>
+template <int kElemBytes, int kHeads, bool kFused>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   using S = DecodeShape<kElemBytes>;
   constexpr int kVec = S::kVec;
@@ -119,6 +127,33 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const int n = a.context_lens[b];
   const int start = s * a.split_tokens;
   const int h0 = g * a.group + hc * kHeads;
+
+  // Fused store: the workgroup of head chunk 0 whose split holds the last
+  // position writes the new row of kv head g to its slot, and every
+  // workgroup whose split reads position n-1 takes that row from the input
+  // instead of the cache (so no workgroup reads a cache row this launch
+  // writes).  The decode-step invariant makes this exactly store-then-decode:
+  // the slot is -1 or the slot of position n-1, in a block no other
+  // sequence reads.
+  int slot_new = -1;
+  u32x4 knew = u32x4{0u, 0u, 0u, 0u}, vnew = u32x4{0u, 0u, 0u, 0u};
+  if constexpr (kFused) {
+    slot_new = a.slot_mapping[b];
+    if (slot_new >= 0) {
+      const int col_ = lane % kCPR;
+      knew = *reinterpret_cast<const u32x4*>(a.k_new + b * a.k_new_stride_bytes +
+                                             (int64_t)g * S::kRowBytes + col_ * 16);
+      vnew = *reinterpret_cast<const u32x4*>(a.v_new + b * a.v_new_stride_bytes +
+                                             (int64_t)g * S::kRowBytes + col_ * 16);
+      const int s_last = n > 0 ? (n - 1) / a.split_tokens : 0;
+      if (hc == 0 && s == s_last && lane < kCPR) {
+        const int64_t off = (((int64_t)(slot_new / kBlockSize) * a.num_kv_heads + g) * kBlockSize +
+                             slot_new % kBlockSize) * S::kRowBytes + lane * 16;
+        *reinterpret_cast<u32x4*>(a.k_cache_w + off) = knew;
+        *reinterpret_cast<u32x4*>(a.v_cache_w + off) = vnew;
+      }
+    }
+  }
   if (start >= n) {
     if (s == 0) {  // empty context: zero output rows
       for (int i = lane; i < kHeads * kCPR; i += 64) {
@@ -165,6 +200,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     const int64_t blk = __builtin_amdgcn_readlane(tab, c0 / kBlockSize - tab_base);
     return ((blk * a.num_kv_heads + g) * kBlockSize + (c0 % kBlockSize)) * S::kRowBytes;
   };
+  // position whose K/V come from the fused store's input (-1: none here)
+  int p_new = -1;
+  if (slot_new >= 0 && n - 1 >= start && n - 1 < end) {
+    const int pos = n - 1;
+    const int blk = __builtin_amdgcn_readlane(tab, pos / kBlockSize - tab_base);
+    if (slot_new == blk * kBlockSize + pos % kBlockSize) p_new = pos;
+  }
 
   // Software pipeline: the next chunk's K is loaded as soon as the current
   // K has been copied to LDS (reusing its registers), the next chunk's V as
@@ -191,6 +233,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       const int r = i * S::kRowsPerLoad + grp;
       k_lds[r * (kCPR + 1) + col] = kr[i];
     }
+    // the fused store's row replaces the cache row (last chunk only; the
+    // later LDS write of the same wave wins)
+    const bool sub = !kPrefetch && p_new >= c0 && p_new < c0 + kTok;  // uniform
+    if (sub && lane < kCPR) k_lds[(p_new - c0) * (kCPR + 1) + lane] = knew;
     __syncthreads();
     if constexpr (kPrefetch) {
 #pragma unroll
@@ -248,6 +294,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     }
     __syncthreads();
 
+    if (sub) {
+#pragma unroll
+      for (int i = 0; i < S::kLoads; ++i)
+        if (i * S::kRowsPerLoad + grp == p_new - c0) vr[i] = vnew;
+    }
     // PV: lane holds kVec dims (column col) of tokens i*kRowsPerLoad + grp
 #pragma unroll
     for (int i = 0; i < S::kLoads; ++i) {
@@ -396,8 +447,12 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 
 template <int kElemBytes, int kHeads>
 void launch_split(const DecodeArgs& args, unsigned grid, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<kElemBytes, kHeads>), dim3(grid), dim3(64), 0, stream,
-                     args);
+  if (args.k_new)
+    hipLaunchKernelGGL((decode_split_kernel<kElemBytes, kHeads, true>), dim3(grid), dim3(64), 0,
+                       stream, args);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<kElemBytes, kHeads, false>), dim3(grid), dim3(64), 0,
+                       stream, args);
 }
 
 template <int kElemBytes>
@@ -474,6 +529,13 @@ static DecodeArgs decode_args(int elem_bytes, const DecodePlan& plan, const Deco
   a.ws_ml = l.workspace
                 ? l.workspace + (size_t)l.batch * l.num_q_heads * plan.nsplit * kHeadDim
                 : nullptr;
+  a.k_new = (const uint8_t*)l.k_new;
+  a.v_new = (const uint8_t*)l.v_new;
+  a.k_new_stride_bytes = l.k_new_stride * elem_bytes;
+  a.v_new_stride_bytes = l.v_new_stride * elem_bytes;
+  a.slot_mapping = l.slot_mapping;
+  a.k_cache_w = (uint8_t*)l.k_cache;
+  a.v_cache_w = (uint8_t*)l.v_cache;
   return a;
 }
 

@@ -44,6 +44,11 @@ struct DecodeLaunch {
   float scale;
   void* out;
   float* workspace;
+  // fused store of this step's rows (decode step); k_new == nullptr: none
+  const void* k_new = nullptr;
+  const void* v_new = nullptr;
+  int64_t k_new_stride = 0, v_new_stride = 0;  // elements between sequences
+  const int32_t* slot_mapping = nullptr;
 };
 
 // The split kernel (partials, and outputs of single-split sequences) and the

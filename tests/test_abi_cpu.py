@@ -82,6 +82,33 @@ def _decode(**kw):
                                 a["wsb"], None)
 
 
+def _step(**kw):
+    a = dict(dtype=BF16, q=FAKE, qs=16 * 128, kn=FAKE, ks=8 * 128, vn=FAKE, vs=8 * 128,
+             slots=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, mb=16, ctx=FAKE, maxctx=4096, batch=4, hq=16,
+             hkv=8, d=128, bs=256, nblk=64, scale=0.088, splits=0, out=FAKE, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    lib = pkv.load_library()
+    return lib.pkv_paged_decode_step(a["dtype"], a["q"], a["qs"], a["kn"], a["ks"], a["vn"],
+                                     a["vs"], a["slots"], a["kc"], a["vc"], a["bt"], a["mb"],
+                                     a["ctx"], a["maxctx"], a["batch"], a["hq"], a["hkv"], a["d"],
+                                     a["bs"], a["nblk"], a["scale"], a["splits"], a["out"], a["ws"],
+                                     a["wsb"], None)
+
+
+def test_decode_step_errors():
+    assert _step(batch=0) == OK
+    assert _step(kn=None) == INVALID
+    assert _step(vn=None) == INVALID
+    assert _step(slots=None) == INVALID
+    assert _step(kn=FAKE + 8) == INVALID      # misaligned
+    assert _step(ks=8 * 128 - 8) == INVALID   # stride below a row
+    assert _step(vs=8 * 128 + 3) == INVALID   # stride not a whole 16-byte chunk
+    assert _step(nblk=0) == INVALID
+    assert _step(hq=24) == UNSUPPORTED
+    assert _step(ws=None, wsb=0) == WORKSPACE
+    assert "k_new" in (_step(kn=None) and pkv.pkv_last_error())
+
+
 def test_decode_errors():
     assert _decode(batch=0) == OK
     assert _decode(batch=-1) == INVALID
