@@ -282,6 +282,36 @@ pkv_status pkv_paged_prefill_varlen(
 size_t pkv_paged_prefill_workspace_bytes(void);
 
 /*
+ * pkv_prefill_varlen -- varlen causal prefill over contiguous fresh k/v, no
+ * cache (source study section 2: without a prefix-cache hit the attention
+ * layer runs varlen attention directly on this step's q, k, v, with
+ * cu_seqlens for queries and keys).  bf16 only.
+ *
+ *   q              device [total_q][num_q_heads][head_dim], row stride
+ *                  q_token_stride elements (as for pkv_paged_prefill_varlen)
+ *   k, v           device [total_k][num_kv_heads][head_dim], row strides
+ *                  k_token_stride / v_token_stride elements (views of a fused
+ *                  qkv buffer are allowed)
+ *   cu_seqlens_q   device int32 [batch + 1]: sequence b's queries are rows
+ *                  cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (n_q of them)
+ *   cu_seqlens_k   device int32 [batch + 1]: its keys are rows
+ *                  cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 (n_k of them)
+ *   max_seqlen_q   host; >= every n_q
+ *   causal         must be 1, bottom-right aligned: query i sees keys
+ *                  0 .. n_k - n_q + i (a query that sees no key gets zeros)
+ *   out, workspace as for pkv_paged_prefill_varlen.
+ * The result is the same as pkv_paged_prefill_varlen over a cache holding
+ * the same keys (same kernel; only the tile source differs).
+ */
+pkv_status pkv_prefill_varlen(
+    pkv_dtype dtype, const void* q, int64_t q_token_stride, const void* k,
+    int64_t k_token_stride, const void* v, int64_t v_token_stride,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+    int32_t max_seqlen_q, int32_t batch, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, float scale, int32_t causal,
+    void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pkv_kv_block_bytes -- bytes of one block of one of K or V for one layer
  * (block_size * num_kv_heads * head_dim * element size); the pages size the
  * cache as a whole number of such blocks ("Dynamische KV-Cache-Allokation").

@@ -6,9 +6,11 @@ package.  The product path (the HIP library and its Python binding) never
 imports it, and this package never imports the product path.
 
 ``ref``   numpy fp64 definitions of the three operations (store, decode,
-          varlen causal prefill) and of the split-K partials and merge.
-``brute`` pure-Python loop versions of decode and prefill for tiny inputs,
-          written independently of ``ref`` to pin it.
+          varlen causal prefill over the cache) and of the split-K partials
+          and merge, plus varlen causal prefill over contiguous k/v.
+``brute`` pure-Python loop versions of decode, prefill and contiguous
+          prefill for tiny inputs, written independently of ``ref`` to pin
+          it.
 
 Parity status: every function here is pinned by CPU tests (brute force,
 library SDPA on contiguous tensors, closed forms, invariants and the worked

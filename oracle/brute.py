@@ -69,3 +69,39 @@ def prefill(q, cache_k, cache_v, cu_seqlens_q, context_lens, block_tables, scale
                 for h in range(hq)
             ]
     return out
+
+
+def prefill_contiguous(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, num_kv_heads):
+    """Keys of sequence b are rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 of
+    k[t][g][d] / v[t][g][d]; query i of n_q sees keys 0 .. n_k - n_q + i."""
+    out = [None] * len(q)
+    for b in range(len(cu_seqlens_q) - 1):
+        qs, qe = cu_seqlens_q[b], cu_seqlens_q[b + 1]
+        ks, ke = cu_seqlens_k[b], cu_seqlens_k[b + 1]
+        n_q, n_k = qe - qs, ke - ks
+        for i in range(n_q):
+            row = []
+            for h in range(len(q[qs + i])):
+                g = h // (len(q[qs + i]) // num_kv_heads)
+                qv = q[qs + i][h]
+                D = len(qv)
+                nkeys = min(n_k, n_k - n_q + i + 1)
+                if nkeys <= 0:
+                    row.append([0.0] * D)
+                    continue
+                scores = []
+                for j in range(nkeys):
+                    acc = 0.0
+                    for d in range(D):
+                        acc += qv[d] * k[ks + j][g][d]
+                    scores.append(acc * scale)
+                top = max(scores)
+                ex = [math.exp(x - top) for x in scores]
+                tot = math.fsum(ex)
+                o = [0.0] * D
+                for j in range(nkeys):
+                    for d in range(D):
+                        o[d] += ex[j] / tot * v[ks + j][g][d]
+                row.append(o)
+            out[qs + i] = row
+    return out

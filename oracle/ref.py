@@ -223,6 +223,40 @@ def merge_partials(acc: np.ndarray, m: np.ndarray, l: np.ndarray) -> np.ndarray:
 # are positions num_cached_tokens .. seqlen - 1)
 # ---------------------------------------------------------------------------
 
+def _prefill_sequence(q: np.ndarray, K: np.ndarray, V: np.ndarray, lo: int, n_q: int, n_k: int,
+                      scale: float, out: np.ndarray, wanted) -> None:
+    """Rows lo .. lo+n_q-1 of ``out`` for one sequence whose keys are K, V
+    ([n_k, Hkv, D]); bottom-right causal.  ``wanted``: None (all rows) or a
+    set of global row indices."""
+    Hq = q.shape[1]
+    Hkv = K.shape[1]
+    idx = [i for i in range(n_q) if wanted is None or (lo + i) in wanted]
+    if not idx:
+        return
+    if wanted is not None:
+        for i in idx:
+            nv = visible_keys(i, n_q, n_k)
+            for h in range(Hq):
+                g = kv_head_of(h, Hq, Hkv)
+                out[lo + i, h], _ = _attend(q[lo + i, h], K[:nv, g, :], V[:nv, g, :], scale)
+        return
+    # all rows of the sequence at once, one head at a time
+    hi = lo + n_q
+    nv = np.array([visible_keys(i, n_q, n_k) for i in range(n_q)])
+    mask = np.arange(n_k)[None, :] < nv[:, None]  # [n_q, n_k]
+    for h in range(Hq):
+        g = kv_head_of(h, Hq, Hkv)
+        S = scale * (q[lo:hi, h, :] @ K[:, g, :].T)
+        S = np.where(mask, S, -np.inf)
+        m = S.max(axis=1, initial=-np.inf)
+        m = np.where(np.isfinite(m), m, 0.0)
+        E = np.where(mask, np.exp(S - m[:, None]), 0.0)
+        L = E.sum(axis=1)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            O = (E @ V[:, g, :]) / L[:, None]
+        out[lo:hi, h] = np.where((nv > 0)[:, None], O, 0.0)
+
+
 def prefill(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
             cu_seqlens_q: np.ndarray, context_lens: np.ndarray,
             block_tables: np.ndarray, scale: float,
@@ -231,37 +265,32 @@ def prefill(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
     Returns out [total_q, Hq, D]; if ``rows`` is given, only those query rows
     are computed (others stay zero) -- used for sampled checks at full size."""
     total_q, Hq, D = q.shape
-    Hkv = k_cache.shape[1]
     out = np.zeros((total_q, Hq, D))
-    batch = len(context_lens)
     wanted = None if rows is None else set(int(r) for r in rows)
-    for b in range(batch):
+    for b in range(len(context_lens)):
         lo, hi = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])
-        n_q, n_k = hi - lo, int(context_lens[b])
-        idx = [i for i in range(n_q) if wanted is None or (lo + i) in wanted]
-        if not idx:
+        n_k = int(context_lens[b])
+        if wanted is not None and not any(lo <= r < hi for r in wanted):
             continue
         K = gather(k_cache, block_tables[b], n_k)
         V = gather(v_cache, block_tables[b], n_k)
-        if wanted is not None:
-            for i in idx:
-                nv = visible_keys(i, n_q, n_k)
-                for h in range(Hq):
-                    g = kv_head_of(h, Hq, Hkv)
-                    out[lo + i, h], _ = _attend(q[lo + i, h], K[:nv, g, :], V[:nv, g, :], scale)
-            continue
-        # all rows of the sequence at once, one head at a time
-        nv = np.array([visible_keys(i, n_q, n_k) for i in range(n_q)])
-        mask = np.arange(n_k)[None, :] < nv[:, None]  # [n_q, n_k]
-        for h in range(Hq):
-            g = kv_head_of(h, Hq, Hkv)
-            S = scale * (q[lo:hi, h, :] @ K[:, g, :].T)
-            S = np.where(mask, S, -np.inf)
-            m = S.max(axis=1, initial=-np.inf)
-            m = np.where(np.isfinite(m), m, 0.0)
-            E = np.where(mask, np.exp(S - m[:, None]), 0.0)
-            L = E.sum(axis=1)
-            with np.errstate(invalid="ignore", divide="ignore"):
-                O = (E @ V[:, g, :]) / L[:, None]
-            out[lo:hi, h] = np.where((nv > 0)[:, None], O, 0.0)
+        _prefill_sequence(q, K, V, lo, hi - lo, n_k, scale, out, wanted)
+    return out
+
+
+def prefill_contiguous(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_seqlens_q: np.ndarray,
+                       cu_seqlens_k: np.ndarray, scale: float,
+                       rows: Optional[Sequence[int]] = None):
+    """Varlen causal prefill without a cache (source study section 2: with
+    no prefix hit the attention layer attends this step's own k, v): keys of
+    sequence b are rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 of k / v
+    ([total_k, Hkv, D] fp64); bottom-right causal as in ``prefill``, so a
+    query that sees no key (n_k < n_q) gets zeros."""
+    total_q, Hq, D = q.shape
+    out = np.zeros((total_q, Hq, D))
+    wanted = None if rows is None else set(int(r) for r in rows)
+    for b in range(len(cu_seqlens_q) - 1):
+        lo, hi = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])
+        k0, k1 = int(cu_seqlens_k[b]), int(cu_seqlens_k[b + 1])
+        _prefill_sequence(q, k[k0:k1], v[k0:k1], lo, hi - lo, k1 - k0, scale, out, wanted)
     return out

@@ -10,7 +10,8 @@ Names follow the C ABI: ``pkv_kv_store``, ``pkv_paged_decode`` (and its two
 halves ``pkv_paged_decode_partials`` / ``pkv_paged_decode_merge``),
 ``pkv_paged_decode_step`` (store fused into decode), ``pkv_paged_decode_workspace_bytes``,
 ``pkv_paged_decode_split_tokens``, ``pkv_paged_prefill_workspace_bytes``,
-``pkv_paged_prefill_varlen``, ``pkv_kv_block_bytes``, ``pkv_last_error``.
+``pkv_paged_prefill_varlen``, ``pkv_prefill_varlen`` (contiguous k/v, no cache),
+``pkv_kv_block_bytes``, ``pkv_last_error``.
 """
 
 from __future__ import annotations
@@ -28,7 +29,7 @@ __all__ = [
     "pkv_paged_decode_step",
     "pkv_paged_decode_workspace_bytes",
     "pkv_paged_decode_split_tokens", "pkv_paged_prefill_varlen",
-    "pkv_paged_prefill_workspace_bytes", "pkv_kv_block_bytes",
+    "pkv_paged_prefill_workspace_bytes", "pkv_prefill_varlen", "pkv_kv_block_bytes",
     "pkv_last_error",
 ]
 
@@ -82,6 +83,10 @@ def load_library() -> ctypes.CDLL:
     lib.pkv_paged_prefill_varlen.argtypes = [c_i32, c_p, c_i64, c_p, c_p, c_p, c_i32, c_p, c_i32,
                                              c_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                              c_i64, c_f, c_i32, c_p, c_p, ctypes.c_size_t, c_p]
+    lib.pkv_prefill_varlen.restype = c_i32
+    lib.pkv_prefill_varlen.argtypes = [c_i32, c_p, c_i64, c_p, c_i64, c_p, c_i64, c_p, c_p, c_i32,
+                                       c_i32, c_i32, c_i32, c_i32, c_f, c_i32, c_p, c_p,
+                                       ctypes.c_size_t, c_p]
     lib.pkv_paged_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.pkv_paged_prefill_workspace_bytes.argtypes = []
     lib.pkv_kv_block_bytes.restype = c_i64
@@ -355,6 +360,47 @@ def pkv_paged_prefill_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: to
                                         int(block_tables.shape[1]), batch, hq, hkv, d, bs, nblk,
                                         float(scale), int(causal), _ptr(out), _ptr(workspace),
                                         ws_bytes, st))
+    return out
+
+
+def pkv_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                       cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_q: int,
+                       scale: float, out: Optional[torch.Tensor] = None, causal: int = 1,
+                       workspace: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    """Varlen causal prefill over contiguous k/v (no cache): q [total_q, Hq, D],
+    k/v [total_k, Hkv, D] (token strides free) -> out [total_q, Hq, D]."""
+    lib = load_library()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _gpu(t, n)
+    _int32(cu_seqlens_q, "cu_seqlens_q")
+    _int32(cu_seqlens_k, "cu_seqlens_k")
+    if q.dtype != k.dtype or v.dtype != k.dtype:
+        raise ValueError("q, k and v must share a dtype")
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("q must be [total_q, Hq, D] and k, v [total_k, Hkv, D]")
+    total, hq, d = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
+    hkv = int(k.shape[1])
+    qs = _rows(q, "q", hq, d)
+    ks = _rows(k, "k", hkv, d)
+    vs = _rows(v, "v", hkv, d)
+    batch = int(cu_seqlens_q.numel()) - 1
+    if batch < 0 or cu_seqlens_k.numel() != batch + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both be [batch + 1]")
+    if out is None:
+        out = torch.empty((total, hq, d), dtype=q.dtype, device=q.device)
+    _gpu(out, "out")
+    if out.shape != (total, hq, d) or not out.is_contiguous() or out.dtype != q.dtype:
+        raise ValueError("out must be a contiguous [total_q, Hq, D] tensor of q's dtype")
+    st = _stream(stream)
+    if workspace is None:
+        workspace = _prefill_workspace(q.device, st)
+    _gpu(workspace, "workspace")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.pkv_prefill_varlen(_dtype_code(q), _ptr(q), qs, _ptr(k), ks, _ptr(v), vs,
+                                  _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), int(max_seqlen_q), batch,
+                                  hq, hkv, d, float(scale), int(causal), _ptr(out),
+                                  _ptr(workspace), ws_bytes, st))
     return out
 
 

@@ -382,4 +382,64 @@ pkv_status pkv_paged_prefill_varlen(pkv_dtype dtype, const void* q, int64_t q_to
 
 size_t pkv_paged_prefill_workspace_bytes(void) { return pkv::prefill_workspace_bytes(); }
 
+pkv_status pkv_prefill_varlen(pkv_dtype dtype, const void* q, int64_t q_token_stride, const void* k,
+                              int64_t k_token_stride, const void* v, int64_t v_token_stride,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int32_t max_seqlen_q, int32_t batch, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, float scale, int32_t causal,
+                              void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (eb == 0) return fail(PKV_ERR_INVALID, "unknown dtype %d", (int)dtype);
+  if (batch < 0 || max_seqlen_q < 0)
+    return fail(PKV_ERR_INVALID, "batch and max_seqlen_q must be >= 0");
+  if (causal != 1) return fail(PKV_ERR_INVALID, "causal must be 1 (got %d)", causal);
+  pkv_status st = check_geometry(num_q_heads, num_kv_heads, head_dim, pkv::kBlockSize);
+  if (st != PKV_OK) return st;
+  if (dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "prefill_varlen supports bf16 only");
+  if (!pkv::prefill_supported_group(num_q_heads / num_kv_heads))
+    return fail(PKV_ERR_UNSUPPORTED, "GQA group size %d is not supported",
+                num_q_heads / num_kv_heads);
+  if (batch == 0 || max_seqlen_q == 0) return PKV_OK;
+  if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_k || !out)
+    return fail(PKV_ERR_INVALID, "null q, k, v, cu_seqlens_q, cu_seqlens_k or out");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(PKV_ERR_INVALID, "q, k, v and out must be 16-byte aligned");
+  if ((st = check_stride("q_token_stride", q_token_stride, (int64_t)num_q_heads * head_dim, eb)) !=
+      PKV_OK)
+    return st;
+  const int64_t kv_row = (int64_t)num_kv_heads * head_dim;
+  if ((st = check_stride("k_token_stride", k_token_stride, kv_row, eb)) != PKV_OK) return st;
+  if ((st = check_stride("v_token_stride", v_token_stride, kv_row, eb)) != PKV_OK) return st;
+  // 64 key rows must stay inside one 32-bit buffer range
+  if (k_token_stride * eb * 64 > INT32_MAX || v_token_stride * eb * 64 > INT32_MAX)
+    return fail(PKV_ERR_UNSUPPORTED, "k/v token stride too large");
+  if (!(scale == scale)) return fail(PKV_ERR_INVALID, "scale is NaN");
+  if (!workspace || ((uintptr_t)workspace & 3) != 0 ||
+      workspace_bytes < pkv::prefill_workspace_bytes())
+    return fail(PKV_ERR_WORKSPACE, "prefill workspace must be non-null, 4-byte aligned and >= %zu bytes",
+                pkv::prefill_workspace_bytes());
+  pkv::PrefillLaunch l;
+  l.q = q;
+  l.q_stride = q_token_stride;
+  l.k_cache = nullptr;
+  l.v_cache = nullptr;
+  l.cu_seqlens_q = cu_seqlens_q;
+  l.max_seqlen_q = max_seqlen_q;
+  l.context_lens = nullptr;
+  l.block_tables = nullptr;
+  l.max_blocks = 0;
+  l.batch = batch;
+  l.num_q_heads = num_q_heads;
+  l.num_kv_heads = num_kv_heads;
+  l.scale = scale;
+  l.out = out;
+  l.workspace = workspace;
+  l.cu_seqlens_k = cu_seqlens_k;
+  l.k_rows = k;
+  l.v_rows = v;
+  l.k_row_stride = k_token_stride;
+  l.v_row_stride = v_token_stride;
+  return hip_status(pkv::launch_prefill(l, (hipStream_t)stream), "prefill_varlen launch");
+}
+
 }  // extern "C"

@@ -77,6 +77,11 @@ struct PrefillLaunch {
   float scale;
   void* out;
   void* workspace;  // prefill_workspace_bytes(), zero on entry, zero on exit
+  // contiguous keys (no cache): cu_seqlens_k != nullptr
+  const int32_t* cu_seqlens_k = nullptr;
+  const void* k_rows = nullptr;
+  const void* v_rows = nullptr;
+  int64_t k_row_stride = 0, v_row_stride = 0;  // elements
 };
 
 size_t prefill_workspace_bytes();

@@ -77,6 +77,13 @@ struct PrefillArgs {
   int32_t heads_per_wg, pos_tiles, head_chunks, max_wg_tiles;
   float scale_log2;
   uint16_t* out;
+  // Keys from contiguous rows instead of the cache (no block table):
+  // sequence b's keys are rows cu_k[b] .. cu_k[b+1]-1 of k_rows / v_rows.
+  // cu_k == nullptr: keys come from the cache through block_tables.
+  const int32_t* cu_k;
+  const uint16_t* k_rows;
+  const uint16_t* v_rows;
+  int64_t k_row_stride, v_row_stride;  // elements between key rows
   int32_t num_items;   // work items: (query tile, sequence, kv head, head chunk)
   int32_t num_queues;  // work queues (one per XCD when the grid allows)
   int32_t* counters;   // [kMaxQueues] queue heads, then the exit count
@@ -111,13 +118,14 @@ __device__ __forceinline__ int v_pos(int key, int c) { return c ^ ((key & 7) << 
 // and wave, so they are computed once (tile_offsets) and a new tile only
 // changes the scalar buffer base.
 template <bool kIsV>
-__device__ __forceinline__ void tile_offsets(uint32_t (&voff)[4], int wave, int lane) {
+__device__ __forceinline__ void tile_offsets(uint32_t (&voff)[4], int wave, int lane,
+                                             uint32_t row_bytes) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int key = wave * 16 + i * 4 + (lane >> 4);
     const int pos = lane & 15;
     const int c = kIsV ? v_pos(key, pos) : k_pos(key, pos);  // the involution maps back
-    voff[i] = (uint32_t)(key * kHeadDim + c * 8) * 2u;
+    voff[i] = (uint32_t)key * row_bytes + (uint32_t)c * 16u;
   }
 }
 
@@ -177,7 +185,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4
 
   const int q_begin = a.cu_q[b];
   const int n_q = a.cu_q[b + 1] - q_begin;
-  const int n_k = a.ctx[b];
+  const int k_begin = a.cu_k ? a.cu_k[b] : 0;
+  const int n_k = a.cu_k ? a.cu_k[b + 1] - k_begin : a.ctx[b];
   const int off = n_k - n_q;
   const int wg_rows = kQT * a.pos_tiles;
   const int wg_tiles = (n_q + wg_rows - 1) / wg_rows;
@@ -217,7 +226,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4
   // every vector memory access in flight, including the copies of the
   // previous tiles.
   const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
-  const int nblk = (wg_kend + kBlockSize - 1) / kBlockSize;
+  const int nblk = a.cu_k ? 0 : (wg_kend + kBlockSize - 1) / kBlockSize;
   const int32_t tab0 = lane < nblk ? table[lane] : 0;
   const int32_t tab1 = lane + 64 < nblk ? table[lane + 64] : 0;
   auto block_at = [&](int i) -> int64_t {  // i uniform
@@ -225,17 +234,29 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4
     if (i < 128) return __builtin_amdgcn_readlane(tab1, i - 64);
     return ((const __attribute__((address_space(4))) int32_t*)table)[i];
   };
+  // key rows of a tile are 256 bytes apart in the cache, a token stride apart
+  // in contiguous k / v
+  const uint32_t k_row_bytes = a.cu_k ? (uint32_t)(a.k_row_stride * 2) : kHeadDim * 2;
+  const uint32_t v_row_bytes = a.cu_k ? (uint32_t)(a.v_row_stride * 2) : kHeadDim * 2;
   uint32_t k_off[4], v_off[4];
-  tile_offsets<false>(k_off, wave & (kGroupWaves - 1), lane);
-  tile_offsets<true>(v_off, wave & (kGroupWaves - 1), lane);
+  tile_offsets<false>(k_off, wave & (kGroupWaves - 1), lane, k_row_bytes);
+  tile_offsets<true>(v_off, wave & (kGroupWaves - 1), lane, v_row_bytes);
   auto issue_copy = [&](int t) {  // group A only
     const int k0 = t * kKT;
-    const int64_t blk = block_at(k0 / kBlockSize);
-    const int64_t base = ((blk * a.num_kv_heads + g) * kBlockSize + (k0 % kBlockSize)) * kHeadDim;
-    const int bytes = min(kKT, n_k - k0) * (kHeadDim * 2);
+    const int nvalid = min(kKT, n_k - k0);
+    const uint16_t *kb, *vb;
+    if (a.cu_k) {
+      kb = a.k_rows + (int64_t)(k_begin + k0) * a.k_row_stride + g * kHeadDim;
+      vb = a.v_rows + (int64_t)(k_begin + k0) * a.v_row_stride + g * kHeadDim;
+    } else {
+      const int64_t blk = block_at(k0 / kBlockSize);
+      const int64_t base = ((blk * a.num_kv_heads + g) * kBlockSize + (k0 % kBlockSize)) * kHeadDim;
+      kb = a.k_cache + base;
+      vb = a.v_cache + base;
+    }
     const int slot = t % kSlots;
-    tile_to_lds(tile_rsrc(a.k_cache + base, bytes), k_off, kbuf[slot], wave);
-    tile_to_lds(tile_rsrc(a.v_cache + base, bytes), v_off, vbuf[slot], wave);
+    tile_to_lds(tile_rsrc(kb, nvalid * (int)k_row_bytes), k_off, kbuf[slot], wave);
+    tile_to_lds(tile_rsrc(vb, nvalid * (int)v_row_bytes), v_off, vbuf[slot], wave);
   };
 
   // PV operand reads (ds_read_b64_tr_b16): in each 16-lane group, lane
@@ -537,6 +558,11 @@ hipError_t launch_prefill(const PrefillLaunch& l, hipStream_t stream) {
   a.num_items = (int32_t)items;
   a.num_queues = std::min(grid, kMaxQueues);
   a.counters = (int32_t*)l.workspace;
+  a.cu_k = l.cu_seqlens_k;
+  a.k_rows = (const uint16_t*)l.k_rows;
+  a.v_rows = (const uint16_t*)l.v_rows;
+  a.k_row_stride = l.k_row_stride;
+  a.v_row_stride = l.v_row_stride;
   hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }

@@ -173,6 +173,31 @@ def test_prefill_errors():
     assert "causal" in (_prefill(causal=2) and pkv.pkv_last_error())
 
 
+def _prefill_contig(**kw):
+    a = dict(dtype=BF16, q=FAKE, qs=32 * 128, k=FAKE, ks=8 * 128, v=FAKE, vs=8 * 128, cuq=FAKE,
+             cuk=FAKE, maxq=100, batch=2, hq=32, hkv=8, d=128, scale=0.088, causal=1, out=FAKE,
+             ws=FAKE, wsb=64)
+    a.update(kw)
+    lib = pkv.load_library()
+    return lib.pkv_prefill_varlen(a["dtype"], a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"],
+                                  a["cuq"], a["cuk"], a["maxq"], a["batch"], a["hq"], a["hkv"],
+                                  a["d"], a["scale"], a["causal"], a["out"], a["ws"], a["wsb"],
+                                  None)
+
+
+def test_prefill_contiguous_errors():
+    assert _prefill_contig(batch=0) == OK
+    assert _prefill_contig(maxq=0) == OK
+    assert _prefill_contig(causal=0) == INVALID
+    assert _prefill_contig(dtype=FP32) == UNSUPPORTED
+    assert _prefill_contig(hq=24) == UNSUPPORTED
+    assert _prefill_contig(cuk=None) == INVALID
+    assert _prefill_contig(k=FAKE + 2) == INVALID
+    assert _prefill_contig(ks=8 * 128 - 8) == INVALID
+    assert _prefill_contig(ws=None) == WORKSPACE
+    assert "cu_seqlens_k" in (_prefill_contig(cuk=None) and pkv.pkv_last_error())
+
+
 def test_prefill_workspace():
     need = pkv.pkv_paged_prefill_workspace_bytes()
     assert 4 <= need <= 256 and need % 4 == 0

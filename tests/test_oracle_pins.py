@@ -204,6 +204,65 @@ def check_sdpa_prefill(seed=0):
     return err
 
 
+def check_sdpa_prefill_contiguous(seed=0):
+    """prefill_contiguous against SDPA with the causal mask is_causal builds
+    itself (square sequences, where top-left and bottom-right alignment
+    coincide), plus an explicit bottom-right mask for n_k > n_q."""
+    rng = np.random.default_rng(seed)
+    Hq, Hkv, D = 8, 2, 16
+    nq = [12, 1, 7, 5]
+    nk = [12, 1, 7, 19]
+    cu_q = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(nk)]).astype(np.int32)
+    q = rng.standard_normal((cu_q[-1], Hq, D))
+    k = rng.standard_normal((cu_k[-1], Hkv, D))
+    v = rng.standard_normal((cu_k[-1], Hkv, D))
+    scale = 1 / math.sqrt(D)
+    got = ref.prefill_contiguous(q, k, v, cu_q, cu_k, scale)
+    err = 0.0
+    for b in range(len(nq)):
+        lo, hi, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        if nq[b] == nk[b]:
+            qt = torch.from_numpy(q[lo:hi]).permute(1, 0, 2)
+            Kt = torch.from_numpy(k[k0:k1]).permute(1, 0, 2).repeat_interleave(Hq // Hkv, dim=0)
+            Vt = torch.from_numpy(v[k0:k1]).permute(1, 0, 2).repeat_interleave(Hq // Hkv, dim=0)
+            want = torch.nn.functional.scaled_dot_product_attention(
+                qt, Kt, Vt, is_causal=True, scale=scale).permute(1, 0, 2).numpy()
+        else:
+            visible = [nk[b] - nq[b] + i + 1 for i in range(nq[b])]
+            want = _sdpa(q[lo:hi], k[k0:k1], v[k0:k1], visible)
+        err = max(err, np.abs(got[lo:hi] - want).max())
+    return err
+
+
+def test_sdpa_prefill_contiguous():
+    assert check_sdpa_prefill_contiguous() < 1e-12
+
+
+def test_brute_force_prefill_contiguous():
+    """Including sequences with fewer keys than queries: the first queries see
+    no key and must be zero."""
+    rng = np.random.default_rng(21)
+    Hq, Hkv, D = 4, 2, 8
+    nq = [5, 3, 6, 1]
+    nk = [5, 7, 2, 1]
+    cu_q = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(nk)]).astype(np.int32)
+    q = rng.standard_normal((cu_q[-1], Hq, D))
+    k = rng.standard_normal((cu_k[-1], Hkv, D))
+    v = rng.standard_normal((cu_k[-1], Hkv, D))
+    got = ref.prefill_contiguous(q, k, v, cu_q, cu_k, 0.3)
+    want = np.array(brute.prefill_contiguous(q.tolist(), k.tolist(), v.tolist(), cu_q.tolist(),
+                                             cu_k.tolist(), 0.3, Hkv))
+    assert np.abs(got - want).max() < 1e-12
+    # sequence 2: 6 queries over 2 keys -- queries 0..3 see nothing
+    assert np.all(got[cu_q[2] : cu_q[2] + 4] == 0.0)
+    assert np.all(np.abs(got[cu_q[2] + 4 : cu_q[3]]) > 0.0)
+    rows = [1, 6, 13]
+    part = ref.prefill_contiguous(q, k, v, cu_q, cu_k, 0.3, rows=rows)
+    assert np.abs(part[rows] - got[rows]).max() < 1e-12
+
+
 def test_sdpa_decode():
     assert check_sdpa_decode() < 1e-12
 
@@ -361,6 +420,14 @@ def test_planted_mistakes_are_caught(monkeypatch):
         orig = ref._attend
         m.setattr(ref, "_attend", lambda q, k, v, s: orig(q, k, v, 1.0))
         assert check_sdpa_decode() > 1e-3
+    with monkeypatch.context() as m:  # contiguous keys: top-left causal alignment
+        m.setattr(ref, "visible_keys", lambda i, nq, nk: min(nk, i + 1))
+        assert check_sdpa_prefill_contiguous() > 1e-3
+    with monkeypatch.context() as m:  # contiguous keys: K and V rows swapped
+        orig_c = ref.prefill_contiguous
+        m.setattr(ref, "prefill_contiguous",
+                  lambda q, k, v, cq, ck, s, rows=None: orig_c(q, v, k, cq, ck, s, rows))
+        assert check_sdpa_prefill_contiguous() > 1e-3
     with monkeypatch.context() as m:  # off-by-one in the number of blocks read
         m.setattr(ref, "num_blocks", lambda n, B: n // B + 1 if n % B else n // B - 1 if n > B else 1)
         with pytest.raises(Exception):
