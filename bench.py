@@ -241,11 +241,11 @@ def time_fused_step(d: Device, steps: int, torch):
 # changes, the figure no longer describes the kernel and is reported as null.
 TRAFFIC = {
     ("decode_split_kernel", "decode-bf16-b64-ctx512-4096-h16-8"): {
-        "bytes": 553420747, "source": "decode.hip",
-        "sha256": "fa1cf29badeef1cb2bb43c8ef93f7e3a57f449caf1f316c7136e3ae49417a86a"},
+        "bytes": 553428083, "source": "decode.hip",
+        "sha256": "84248992c6af5fc9ba6aa48e1583d07309286d2599f3bca2a67eb4f240776112"},
     ("prefill_kernel", "prefill-bf16-8seq-L1024-4096-prefix512-h32-8"): {
-        "bytes": 1969540924, "source": "prefill.hip",
-        "sha256": "cbc1fd99f520dbaf0daf75e06331ab959e9061e09e022b140508ff4981d22943"},
+        "bytes": 1898145669, "source": "prefill.hip",
+        "sha256": "09b3f3c2a32cd60d5ca2345306c8fead9803aaba19b7e9ed0c8d5b919030be50"},
 }
 
 
@@ -260,6 +260,51 @@ def traffic_for(kernel: str, workload: str):
         if hashlib.sha256(f.read()).hexdigest() != rec["sha256"]:
             return None
     return rec["bytes"]
+
+
+def time_contiguous_prefill(d: Device, steps: int, torch):
+    """pkv_prefill_varlen (keys from contiguous rows, no block table) on the
+    same keys as the paged prefill: every context row gathered once from the
+    cache (after the store) into [total_k, Hkv, D].  Mean event-timed ms,
+    MALL evicted before each launch."""
+    import numpy as np
+
+    import paged_kv_cache_325_amd as pkv
+
+    w = d.w
+    blk, row = [], []
+    for b in range(w.batch):
+        j = np.arange(int(w.context_lens[b]))
+        blk.append(w.block_tables[b][j // w.block_size])
+        row.append(j % w.block_size)
+    blk = torch.from_numpy(np.concatenate(blk).astype(np.int64)).cuda()
+    row = torch.from_numpy(np.concatenate(row).astype(np.int64)).cuda()
+    d.store()
+    k = d.k_cache[blk, :, row, :].contiguous()
+    v = d.v_cache[blk, :, row, :].contiguous()
+    cu_k = torch.from_numpy(
+        np.concatenate([[0], np.cumsum(w.context_lens)]).astype(np.int32)).cuda()
+    out = torch.empty_like(d.out)
+
+    def run():
+        pkv.pkv_prefill_varlen(d.q, k, v, d.cu_seqlens_q, cu_k, w.max_seqlen_q, w.scale, out=out)
+
+    flush = make_flush(torch)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        flush()
+        run()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for e0, e1 in evs:
+        flush()
+        e0.record(stream)
+        run()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    del flush, k, v
+    return mean([e0.elapsed_time(e1) for e0, e1 in evs])
 
 
 def measure(index: int, steps: int, warmup: int, torch, settle_s: float):
@@ -295,6 +340,8 @@ def measure(index: int, steps: int, warmup: int, torch, settle_s: float):
     else:
         r["flops"] = w.prefill_flops()
         r["tflops"] = r["flops"] / (r["attn_ms"] * 1e-3) / 1e12
+        r["contiguous_ms"] = time_contiguous_prefill(d, max(5, steps // 2), torch)
+        r["contiguous_tflops"] = r["flops"] / (r["contiguous_ms"] * 1e-3) / 1e12
         # prefill reads each unique cached K/V byte at least once
         r["attn_bytes"] = w.unique_kv_bytes() + w.qo_bytes()
     r["step_bytes"] = w.store_bytes() + r["attn_bytes"]
@@ -405,7 +452,9 @@ def main() -> int:
             if "tflops" in r:
                 e.update(prefill_tflops=round(r["tflops"], 1),
                          mfma_frac=round(r["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
-                         prefill_tokens_per_s=round(r["w"].num_tokens / (r["attn_ms"] * 1e-3), 1))
+                         prefill_tokens_per_s=round(r["w"].num_tokens / (r["attn_ms"] * 1e-3), 1),
+                         contiguous_kv_ms=round(r["contiguous_ms"], 4),
+                         contiguous_kv_tflops=round(r["contiguous_tflops"], 1))
             else:
                 e.update(decode_gbs=round(r["attn_gbs"], 1),
                          hbm_frac=round(r["attn_gbs"] / HBM_PEAK_GBS, 4),
