@@ -75,7 +75,8 @@ typedef enum {
   PKV_ERR_INVALID = 1,
   PKV_ERR_UNSUPPORTED = 2,
   PKV_ERR_WORKSPACE = 3,
-  PKV_ERR_HIP = 4
+  PKV_ERR_HIP = 4,
+  PKV_ERR_NO_BLOCKS = 5 /* block manager: not enough free blocks (pkv_block_manager.h) */
 } pkv_status;
 
 typedef enum { PKV_FP32 = 0, PKV_BF16 = 1 } pkv_dtype;

@@ -2,8 +2,9 @@
 
     python -m paged_kv_cache_325_amd.build [--debug]
 
-Each ``csrc/*.hip`` file is compiled to an object under ``_build/`` in
-parallel, then linked into ``paged_kv_cache_325_amd/libpkv.so``.  Packed-fp32
+Each ``csrc/*.hip`` file (hipcc) and each host-only ``csrc/*.cpp`` file (g++)
+is compiled to an object under ``_build/`` in parallel, then linked into
+``paged_kv_cache_325_amd/libpkv.so``.  Packed-fp32
 VALU instructions are disabled for device code.
 """
 
@@ -29,6 +30,13 @@ def hipcc() -> str:
     exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(exe):
         raise RuntimeError("hipcc not found; the ROCm toolchain is required to build libpkv")
+    return exe
+
+
+def gxx() -> str:
+    exe = shutil.which("g++")
+    if not exe:
+        raise RuntimeError("g++ not found; it builds the host-only C++ sources of libpkv")
     return exe
 
 
@@ -70,8 +78,20 @@ def build(debug: bool = False, verbose: bool = False) -> str:
             sys.stderr.write(r.stderr)
         return obj
 
-    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(compile_one, srcs))
+    def compile_host(src):
+        # host-only C++ (the block manager): no device code, plain g++
+        obj = os.path.join(BUILD_DIR, os.path.basename(src)[:-4] + ".host.o")
+        cmd = [gxx(), "-std=c++17", "-fPIC", "-O2", "-Wall", f"-I{INCLUDE}", "-c", src, "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        return obj
+
+    host_srcs = sorted(glob.glob(os.path.join(CSRC, "*.cpp")))
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(host_srcs))) as ex:
+        futs = [ex.submit(compile_one, s) for s in srcs] + [ex.submit(compile_host, s)
+                                                          for s in host_srcs]
+        objs = [f.result() for f in futs]
     tmp = LIB + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

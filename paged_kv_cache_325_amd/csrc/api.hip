@@ -7,13 +7,15 @@
 #include <string>
 
 #include "pkv.h"
+#include "pkv_error.h"
 #include "pkv_internal.h"
 
+namespace pkv {
+
 namespace {
-
 thread_local std::string g_last_error;
+}  // namespace
 
-pkv_status fail(pkv_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 pkv_status fail(pkv_status st, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -23,6 +25,14 @@ pkv_status fail(pkv_status st, const char* fmt, ...) {
   g_last_error = buf;
   return st;
 }
+
+const char* last_error() { return g_last_error.c_str(); }
+
+}  // namespace pkv
+
+namespace {
+
+using pkv::fail;
 
 pkv_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return PKV_OK;
@@ -66,7 +76,7 @@ pkv_status check_stride(const char* name, int64_t stride, int64_t min_elems, int
 
 extern "C" {
 
-const char* pkv_last_error(void) { return g_last_error.c_str(); }
+const char* pkv_last_error(void) { return pkv::last_error(); }
 
 int64_t pkv_kv_block_bytes(pkv_dtype dtype, int32_t num_kv_heads, int32_t head_dim,
                            int32_t block_size) {

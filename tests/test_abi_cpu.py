@@ -3,6 +3,7 @@ declares, and rejects bad host arguments with the documented status before
 touching HIP (no kernel is launched here)."""
 
 import ctypes
+import glob
 import os
 import re
 
@@ -11,7 +12,6 @@ import pytest
 import paged_kv_cache_325_amd as pkv
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pkv.h")
 
 BF16, FP32 = pkv.PKV_BF16, pkv.PKV_FP32
 OK, INVALID, UNSUPPORTED, WORKSPACE = pkv.PKV_OK, pkv.PKV_ERR_INVALID, pkv.PKV_ERR_UNSUPPORTED, pkv.PKV_ERR_WORKSPACE
@@ -21,15 +21,19 @@ FAKE = 0x10000
 
 
 def _declared_symbols():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+    """Every function declared in include/*.h."""
+    syms = set()
+    for name in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        syms |= set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", open(name).read()))
+    return sorted(syms)
 
 
 def test_library_exports_every_declared_symbol():
     lib = pkv.load_library()
     syms = _declared_symbols()
     assert set(syms) >= {"pkv_kv_store", "pkv_paged_decode", "pkv_paged_prefill_varlen",
-                         "pkv_paged_decode_workspace_bytes", "pkv_last_error"}
+                         "pkv_paged_decode_workspace_bytes", "pkv_last_error",
+                         "pkv_bm_allocate", "pkv_bm_may_append", "pkv_bm_build_decode"}
     for s in syms:
         assert hasattr(lib, s), s
     # and nm agrees that they are exported C symbols
