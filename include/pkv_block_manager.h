@@ -155,6 +155,22 @@ pkv_status pkv_bm_build_decode(const pkv_block_manager* bm, const int64_t* seq_i
                                int32_t* positions, int32_t* slot_mapping, int32_t* context_lens,
                                int32_t* block_tables, int32_t* max_context_len);
 
+/* Batch forms of one engine step's host work (one call per step instead of
+ * one per sequence; the same results as the per-sequence calls in order).
+ * pkv_bm_append_tokens: append_token(seq_ids[i], token_ids[i]) for each i.
+ * pkv_bm_decode_step: may_append for each listed sequence (in order), then
+ * pkv_bm_build_decode over them.  A sequence may be listed once.  Every
+ * check (ids, states, width, and the number of new blocks the step needs
+ * against the free blocks: PKV_ERR_NO_BLOCKS) runs before anything changes,
+ * so the scheduler preempts and retries on failure as it would after
+ * can_append. */
+pkv_status pkv_bm_append_tokens(pkv_block_manager* bm, const int64_t* seq_ids, int32_t num_seqs,
+                                const int32_t* token_ids);
+pkv_status pkv_bm_decode_step(pkv_block_manager* bm, const int64_t* seq_ids, int32_t num_seqs,
+                              int32_t width, int32_t* input_ids, int32_t* positions,
+                              int32_t* slot_mapping, int32_t* context_lens,
+                              int32_t* block_tables, int32_t* max_context_len);
+
 #ifdef __cplusplus
 }
 #endif

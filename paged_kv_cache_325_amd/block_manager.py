@@ -49,6 +49,9 @@ def _lib():
                                           _c_p, _c_p, _c_p, _P_I32, _P_I32]),
         "pkv_bm_build_decode": (_c_i32, [_c_p, _c_p, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p,
                                          _c_p, _P_I32]),
+        "pkv_bm_append_tokens": (_c_i32, [_c_p, _c_p, _c_i32, _c_p]),
+        "pkv_bm_decode_step": (_c_i32, [_c_p, _c_p, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p,
+                                        _c_p, _P_I32]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -177,6 +180,21 @@ class BlockManager:
                 "max_seqlen_k": mk.value, "block_tables": tables}
 
     def build_decode(self, seq_ids, width: int | None = None) -> dict:
+        return self._decode(self._lib.pkv_bm_build_decode, seq_ids, width)
+
+    # batch forms of one engine step
+    def append_tokens(self, seq_ids, token_ids) -> None:
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        t = _i32(token_ids)
+        if t.size != ids.size:
+            raise ValueError("one token per sequence")
+        _check(self._lib.pkv_bm_append_tokens(self._h, _ptr(ids), ids.size, _ptr(t)))
+
+    def decode_step(self, seq_ids, width: int) -> dict:
+        """may_append for each sequence, then build_decode (pkv_bm_decode_step)."""
+        return self._decode(self._lib.pkv_bm_decode_step, seq_ids, width)
+
+    def _decode(self, fn, seq_ids, width):
         ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
         if width is None:
             width = max((self.sequence(int(i))[2] for i in ids), default=0)
@@ -184,8 +202,7 @@ class BlockManager:
         input_ids, positions, slots, ctx = (np.empty(n, np.int32) for _ in range(4))
         tables = np.empty((n, width), np.int32)
         mk = ctypes.c_int32()
-        _check(self._lib.pkv_bm_build_decode(
-            self._h, _ptr(ids), n, width, _ptr(input_ids), _ptr(positions), _ptr(slots),
-            _ptr(ctx), _ptr(tables), ctypes.byref(mk)))
+        _check(fn(self._h, _ptr(ids), n, width, _ptr(input_ids), _ptr(positions), _ptr(slots),
+                  _ptr(ctx), _ptr(tables), ctypes.byref(mk)))
         return {"input_ids": input_ids, "positions": positions, "slot_mapping": slots,
                 "context_lens": ctx, "max_context_len": mk.value, "block_tables": tables}

@@ -57,6 +57,7 @@ struct Sequence {
   std::vector<int32_t> tokens;
   std::vector<int32_t> table;
   int32_t num_cached_tokens = 0;
+  uint64_t stamp = 0;  // last batch call that listed it (duplicate check)
 
   int32_t len() const { return (int32_t)tokens.size(); }
 };
@@ -81,6 +82,7 @@ struct pkv_block_manager {
   uint64_t ht_mask = 0;
   size_t ht_used = 0;  // occupied slots, live or stale
   std::unordered_map<int64_t, Sequence> seqs;
+  uint64_t batch_calls = 0;
 
   int32_t nblocks_of(int32_t len) const { return (len + block_size - 1) / block_size; }
 
@@ -199,6 +201,43 @@ pkv_status check_batch(const pkv_block_manager* bm, const int64_t* ids, int32_t 
     (*out)[i] = s;
   }
   return PKV_OK;
+}
+
+// may_append's checks: *need = 1 when the sequence's newest token opens a
+// block.  Called once per appended token, the table is one block short
+// exactly then; a table that already covers the length needs nothing.
+pkv_status check_growth(const pkv_block_manager* bm, const Sequence& s, int64_t seq_id,
+                        int32_t* need) {
+  if (s.table.empty())
+    return fail(PKV_ERR_INVALID, "sequence %lld holds no blocks (allocate first)",
+                (long long)seq_id);
+  const int32_t nb = bm->nblocks_of(s.len());
+  const int32_t nt = (int32_t)s.table.size();
+  const bool opens = s.len() % bm->block_size == 1 && nt == nb - 1;
+  if (!opens && nt != nb)
+    return fail(PKV_ERR_INVALID,
+                "sequence %lld: %d tokens but %d blocks (one may_append per appended token)",
+                (long long)seq_id, s.len(), nt);
+  *need = opens ? 1 : 0;
+  return PKV_OK;
+}
+
+// may_append's effect, once check_growth passed and a free block is there if
+// one is needed.
+void grow(pkv_block_manager* bm, Sequence* s) {
+  const int32_t B = bm->block_size;
+  const int32_t nb = bm->nblocks_of(s->len());
+  const int32_t nt = (int32_t)s->table.size();
+  const int32_t r = s->len() % B;
+  if (r == 1 && nt == nb - 1) {  // the new token opens a block
+    s->table.push_back(bm->take_block(bm->head));
+  } else if (r == 0 && bm->hash[s->table.back()] == -1) {
+    // the new token fills the last block: hash and register it
+    const int32_t last = s->table.back();
+    const int64_t prefix = nt > 1 ? bm->hash[s->table[nb - 2]] : -1;
+    const int32_t* toks = s->tokens.data() + (size_t)(nb - 1) * B;
+    bm->register_block(last, chain_hash(toks, B, prefix), toks);
+  }
 }
 
 void write_table(const Sequence& s, int32_t width, int32_t* row) {
@@ -346,32 +385,11 @@ pkv_status pkv_bm_can_append(const pkv_block_manager* bm, int64_t seq_id, int32_
 pkv_status pkv_bm_may_append(pkv_block_manager* bm, int64_t seq_id) {
   Sequence* s = nullptr;
   if (pkv_status st = find_seq(bm, seq_id, &s)) return st;
-  if (s->table.empty())
-    return fail(PKV_ERR_INVALID, "sequence %lld holds no blocks (allocate first)",
-                (long long)seq_id);
-  const int32_t B = bm->block_size;
-  const int32_t nb = bm->nblocks_of(s->len());
-  const int32_t nt = (int32_t)s->table.size();
-  const int32_t r = s->len() % B;
-  // Called once per appended token, the table is one block short exactly
-  // when the new token opens a block.  A call whose table already covers the
-  // length (a second call, or one right after allocate) changes nothing.
-  const bool opens = r == 1 && nt == nb - 1;
-  if (!opens && nt != nb)
-    return fail(PKV_ERR_INVALID,
-                "sequence %lld: %d tokens but %d blocks (one may_append per appended token)",
-                (long long)seq_id, s->len(), nt);
-  if (opens) {  // the new token opens a block
-    if (bm->nfree < 1)
-      return fail(PKV_ERR_NO_BLOCKS, "sequence %lld needs a block, none free", (long long)seq_id);
-    s->table.push_back(bm->take_block(bm->head));
-  } else if (r == 0 && bm->hash[s->table.back()] == -1) {
-    // the new token fills the last block: hash and register it
-    const int32_t last = s->table.back();
-    const int64_t prefix = nt > 1 ? bm->hash[s->table[nb - 2]] : -1;
-    const int32_t* toks = s->tokens.data() + (size_t)(nb - 1) * B;
-    bm->register_block(last, chain_hash(toks, B, prefix), toks);
-  }
+  int32_t need = 0;
+  if (pkv_status st = check_growth(bm, *s, seq_id, &need)) return st;
+  if (bm->nfree < need)
+    return fail(PKV_ERR_NO_BLOCKS, "sequence %lld needs a block, none free", (long long)seq_id);
+  grow(bm, s);
   return PKV_OK;
 }
 
@@ -501,6 +519,53 @@ pkv_status pkv_bm_build_decode(const pkv_block_manager* bm, const int64_t* seq_i
   }
   if (max_context_len) *max_context_len = mk;
   return PKV_OK;
+}
+
+pkv_status pkv_bm_append_tokens(pkv_block_manager* bm, const int64_t* seq_ids, int32_t num_seqs,
+                                const int32_t* token_ids) {
+  if (!bm) return fail(PKV_ERR_INVALID, "null block manager");
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID, "num_seqs (%d) < 0", num_seqs);
+  if (num_seqs > 0 && (!seq_ids || !token_ids))
+    return fail(PKV_ERR_INVALID, "seq_ids or token_ids is null");
+  std::vector<Sequence*> seqs(num_seqs);
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    if (pkv_status st = find_seq(bm, seq_ids[i], &seqs[i])) return st;
+    if (seqs[i]->len() == 0x7fffffff)
+      return fail(PKV_ERR_INVALID, "sequence %lld is at the int32 limit", (long long)seq_ids[i]);
+  }
+  for (int32_t i = 0; i < num_seqs; ++i) seqs[i]->tokens.push_back(token_ids[i]);
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_decode_step(pkv_block_manager* bm, const int64_t* seq_ids, int32_t num_seqs,
+                              int32_t width, int32_t* input_ids, int32_t* positions,
+                              int32_t* slot_mapping, int32_t* context_lens,
+                              int32_t* block_tables, int32_t* max_context_len) {
+  if (!bm) return fail(PKV_ERR_INVALID, "null block manager");
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID, "num_seqs (%d) < 0", num_seqs);
+  if (num_seqs > 0 && !seq_ids) return fail(PKV_ERR_INVALID, "seq_ids is null");
+  if (num_seqs > 0 && (!slot_mapping || !context_lens || !block_tables))
+    return fail(PKV_ERR_INVALID, "an output array is null");
+  std::vector<Sequence*> seqs(num_seqs);
+  int32_t need = 0;
+  const uint64_t stamp = ++bm->batch_calls;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    if (pkv_status st = find_seq(bm, seq_ids[i], &seqs[i])) return st;
+    if (seqs[i]->stamp == stamp)
+      return fail(PKV_ERR_INVALID, "sequence %lld listed twice", (long long)seq_ids[i]);
+    seqs[i]->stamp = stamp;
+    int32_t n1 = 0;
+    if (pkv_status st = check_growth(bm, *seqs[i], seq_ids[i], &n1)) return st;
+    need += n1;
+    if (width < bm->nblocks_of(seqs[i]->len()))
+      return fail(PKV_ERR_INVALID, "width %d < table length %d", width,
+                  bm->nblocks_of(seqs[i]->len()));
+  }
+  if (bm->nfree < need)
+    return fail(PKV_ERR_NO_BLOCKS, "the step needs %d new blocks, %d free", need, bm->nfree);
+  for (Sequence* s : seqs) grow(bm, s);
+  return pkv_bm_build_decode(bm, seq_ids, num_seqs, width, input_ids, positions, slot_mapping,
+                             context_lens, block_tables, max_context_len);
 }
 
 }  // extern "C"

@@ -128,6 +128,65 @@ class LibAdapter:
         return self.bm.build_decode([self._id(s) for s in sids], width)
 
 
+class LibBatchAdapter(LibAdapter):
+    """The library driven through its batch calls: appended tokens are
+    flushed with one pkv_bm_append_tokens, and a decode step's may_append
+    calls are deferred into one pkv_bm_decode_step.  can_append counts the
+    blocks the deferred calls will take (frees only ever append to the back
+    of the free list, so deferring the front pops changes no outcome)."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        super().__init__(num_blocks, block_size)
+        self.block_size = block_size
+        self.appends: list = []
+        self.pending: list = []
+        self.pending_need = 0
+
+    def _flush(self):
+        if self.appends:
+            ids, toks = zip(*self.appends)
+            self.bm.append_tokens([self._id(s) for s in ids], list(toks))
+            self.appends = []
+
+    def append(self, sid, token):
+        self.appends.append((sid, token))
+
+    def _need(self, sid):
+        n, _, nt = self.bm.sequence(self._id(sid))
+        return 1 if n % self.block_size == 1 and nt == -(-n // self.block_size) - 1 else 0
+
+    def can_append(self, sid):
+        self._flush()
+        return self.bm.num_free_blocks() - self.pending_need >= self._need(sid)
+
+    def may_append(self, sid):
+        self._flush()
+        self.pending.append(sid)
+        self.pending_need += self._need(sid)
+
+    def decode_meta(self, sids, width):
+        self._flush()
+        assert list(sids) == self.pending, "a decode step lists the sequences grown for it"
+        meta = self.bm.decode_step([self._id(s) for s in sids], width)
+        self.pending, self.pending_need = [], 0
+        return meta
+
+
+    def deallocate(self, sid):  # preemption happens between deferred growths
+        self._flush()
+        assert sid not in self.pending
+        LibAdapter.deallocate(self, sid)
+
+
+for _name in ("remove", "can_allocate", "allocate", "table", "cached", "length", "free",
+              "block", "prefill_meta"):
+    def _flushing(self, *args, _f=getattr(LibAdapter, _name)):
+        self._flush()
+        assert not self.pending, "only a decode step may follow deferred growth"
+        return _f(self, *args)
+    setattr(LibBatchAdapter, _name, _flushing)
+
+
 def as_plain(meta: dict) -> dict:
     out = {}
     for k, v in meta.items():

@@ -11,7 +11,8 @@ import pytest
 import paged_kv_cache_325_amd as pkv
 from oracle import block_manager as obm
 from paged_kv_cache_325_amd.block_manager import BlockManager, pkv_block_hash
-from tests.bm_scenario import LibAdapter, OracleAdapter, run_golden, run_stream
+from tests.bm_scenario import (LibAdapter, LibBatchAdapter, OracleAdapter, run_golden,
+                                run_stream)
 from workloads.requests import request_stream
 
 INVALID, NO_BLOCKS = pkv.PKV_ERR_INVALID, 5
@@ -45,6 +46,37 @@ def test_streams_in_lockstep(seed, block_size, num_blocks, vocab):
                                                                           block_size)],
                        reqs, seed, num_blocks)
     assert stats["finished"] == len(reqs) and stats["cached_tokens"] > 0
+
+
+@pytest.mark.parametrize("seed,block_size,num_blocks,vocab", [(41, 4, 12, 4), (42, 8, 16, 3)])
+def test_batch_calls_in_lockstep(seed, block_size, num_blocks, vocab):
+    # pkv_bm_append_tokens / pkv_bm_decode_step against the oracle's
+    # per-sequence calls and the library's own per-sequence calls
+    reqs = request_stream(seed, 40, block_size, vocab=vocab,
+                          max_suffix=3 * block_size, max_decode=3 * block_size)
+    stats = run_stream([OracleAdapter(num_blocks, block_size),
+                        LibAdapter(num_blocks, block_size),
+                        LibBatchAdapter(num_blocks, block_size)], reqs, seed, num_blocks)
+    assert stats["finished"] == len(reqs) and stats["preemptions"] > 0
+
+
+def test_decode_step_checks_before_changing_anything():
+    m = BlockManager(3, 4)
+    m.add_sequence(1, [1, 2, 3, 4])
+    m.add_sequence(2, [5, 6, 7, 8])
+    m.allocate(1)
+    m.allocate(2)                                  # one block free
+    m.append_tokens([1, 2], [9, 9])                # both open a block: 2 needed
+    before = _state(m, [1, 2])
+    assert _status(lambda: m.decode_step([1, 2], 2)) == NO_BLOCKS
+    assert _status(lambda: m.decode_step([1, 1], 2)) == INVALID   # listed twice
+    assert _status(lambda: m.decode_step([1], 1)) == INVALID      # width 1 < 2 blocks
+    assert _status(lambda: m.decode_step([1, 77], 2)) == INVALID  # unknown id
+    assert _status(lambda: m.append_tokens([1, 77], [0, 0])) == INVALID
+    assert _state(m, [1, 2]) == before
+    meta = m.decode_step([2], 2)
+    assert meta["slot_mapping"].tolist() == [2 * 4 + 0] and meta["context_lens"].tolist() == [5]
+    assert m.block_table(2) == [1, 2] and m.num_free_blocks() == 0
 
 
 @pytest.mark.slow
