@@ -28,6 +28,8 @@ algorithmic bytes per launch over its mean event-timed duration, against the
 8 TB/s HBM peak.  ``cpu_baseline`` times the CPU oracle on the same workload
 (bounded to ~10 s, one thread).  ``extra`` reports the other workloads with
 the same method (prefill against the 2.5 PFLOP/s dense bf16 MFMA peak), and
+the same decode and prefill with cache blocks of 16, 32, 64 and 1024 tokens
+(``block-size-study``: attention time and fragmentation), and
 the host time of the block manager (C++ through the binding) for one decode
 step of 256 sequences and one prefill admission of 8 prompts; the oracle's
 time for the same appears under ``cpu_baseline.block_manager``.
@@ -405,6 +407,45 @@ def cpu_baseline(index: int, budget_s: float = 10.0):
     }
 
 
+BLOCK_SIZE_STUDY = (16, 32, 64, 1024)
+
+
+def time_block_sizes(torch, steps: int = 10, warmup: int = 3) -> dict:
+    """Gather efficiency against fragmentation: the 64-sequence decode and
+    the prefill workload drawn with other cache block sizes (same lengths,
+    same sharing in tokens), attention timed as in time_steps; fragmentation
+    = unused share of the rows of the blocks the contexts occupy."""
+    import dataclasses
+
+    import numpy as np
+
+    from workloads import build, config_specs
+
+    out = {}
+    for index in (2, 3):
+        for B in BLOCK_SIZE_STUDY:
+            spec, rng = config_specs(index)
+            shared = [x * 256 // B for x in spec.shared_blocks] if spec.shared_blocks else None
+            w = build(dataclasses.replace(spec, block_size=B, shared_blocks=shared), rng)
+            d = Device(w, torch)
+            d.check()
+            _, part_ms, _ = time_steps(d, steps, warmup, torch, 0.3)
+            attn_ms = mean([sum(x) for x in zip(*part_ms)])
+            blocks = int((-(-w.context_lens.astype(np.int64) // B)).sum())
+            e = {"attn_ms": round(attn_ms, 4),
+                 "fragmentation": round(1 - float(w.context_lens.sum()) / (blocks * B), 4)}
+            if w.spec.mode == "decode":
+                e["decode_gbs"] = round((w.logical_kv_bytes() + w.qo_bytes()) /
+                                        (attn_ms * 1e-3) / 1e9, 1)
+            else:
+                e["prefill_tflops"] = round(w.prefill_flops() / (attn_ms * 1e-3) / 1e12, 1)
+            out[f"{w.spec.name}@B{B}"] = e
+            log(f"block size {B}, workload {index}: {e}")
+            del d
+            torch.cuda.empty_cache()
+    return out
+
+
 # Host block manager: one engine step's bookkeeping at the shapes of the
 # 256-sequence decode workload (contexts U[1024, 8192]) and of the prefill
 # workload (8 prompts of U[1024, 4096] tokens behind a shared 512-token
@@ -589,6 +630,8 @@ def main() -> int:
                 "mean_launch_ms": round(head["attn_ms"], 5)}
 
     if not args.no_extra:
+        log("timing other cache block sizes")
+        extra["block-size-study"] = time_block_sizes(torch)
         log("timing the host block manager")
         extra["block-manager-host"] = time_block_manager()
 

@@ -57,8 +57,10 @@ pkv_status check_geometry(int32_t num_q_heads, int32_t num_kv_heads, int32_t hea
                 block_size);
   if (head_dim != pkv::kHeadDim)
     return fail(PKV_ERR_UNSUPPORTED, "head_dim %d is not supported (only 128)", head_dim);
-  if (block_size != pkv::kBlockSize)
-    return fail(PKV_ERR_UNSUPPORTED, "block_size %d is not supported (only 256)", block_size);
+  if (!pkv::block_size_supported(block_size))
+    return fail(PKV_ERR_UNSUPPORTED,
+                "block_size %d is not supported (16, 32, or a multiple of 64 up to %d)",
+                block_size, pkv::kMaxBlockSize);
   return PKV_OK;
 }
 
@@ -109,7 +111,7 @@ pkv_status pkv_kv_store(pkv_dtype dtype, const void* k, int64_t k_token_stride, 
     return fail(PKV_ERR_UNSUPPORTED, "num_blocks * block_size exceeds the int32 slot range");
   return hip_status(pkv::launch_kv_store(eb, k, k_token_stride, v, v_token_stride, k_cache,
                                          v_cache, slot_mapping, num_tokens, num_kv_heads,
-                                         (hipStream_t)stream),
+                                         block_size, (hipStream_t)stream),
                     "kv_store launch");
 }
 
@@ -118,8 +120,9 @@ static bool decode_plan_for(int32_t batch, int32_t num_q_heads, int32_t num_kv_h
                             int32_t num_splits, pkv::DecodePlan* plan) {
   if (batch < 0 || max_context_len < 0 || num_splits < 0) return false;
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads) return false;
-  if (head_dim != pkv::kHeadDim || block_size != pkv::kBlockSize) return false;
-  return pkv::plan_decode(batch, num_q_heads, num_kv_heads, max_context_len, num_splits, plan);
+  if (head_dim != pkv::kHeadDim || !pkv::block_size_supported(block_size)) return false;
+  return pkv::plan_decode(batch, num_q_heads, num_kv_heads, max_context_len, num_splits,
+                          block_size, plan);
 }
 
 size_t pkv_paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
@@ -177,7 +180,8 @@ pkv_status check_decode_common(pkv_dtype dtype, int32_t batch, int32_t num_q_hea
   if (!context_lens || !out)
     return fail(PKV_ERR_INVALID, "null context_lens or out with batch = %d", batch);
   if (!aligned16(out)) return fail(PKV_ERR_INVALID, "out must be 16-byte aligned");
-  if (!pkv::plan_decode(batch, num_q_heads, num_kv_heads, max_context_len, num_splits, plan))
+  if (!pkv::plan_decode(batch, num_q_heads, num_kv_heads, max_context_len, num_splits,
+                        block_size, plan))
     return fail(PKV_ERR_UNSUPPORTED, "no decode plan for these arguments");
   if (workspace_bytes < plan->workspace_bytes || (plan->workspace_bytes && !workspace))
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
@@ -248,6 +252,7 @@ pkv_status decode_parts(int parts, pkv_dtype dtype, const void* q, int64_t q_tok
   l.batch = batch;
   l.num_q_heads = num_q_heads;
   l.num_kv_heads = num_kv_heads;
+  l.block_size = block_size;
   l.scale = scale;
   l.out = out;
   l.workspace = plan.workspace_bytes ? (float*)workspace : nullptr;
@@ -384,6 +389,7 @@ pkv_status pkv_paged_prefill_varlen(pkv_dtype dtype, const void* q, int64_t q_to
   l.batch = batch;
   l.num_q_heads = num_q_heads;
   l.num_kv_heads = num_kv_heads;
+  l.block_size = block_size;
   l.scale = scale;
   l.out = out;
   l.workspace = workspace;

@@ -42,6 +42,8 @@
 // the context's K and V bytes plus q and out.
 #include <math.h>
 
+#include <algorithm>
+
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -50,7 +52,6 @@ namespace pkv {
 namespace {
 
 constexpr int kTargetWaves = 256 * 32;  // 256 CUs; enough waves for balance
-constexpr int kMaxSplitTokens = 64 * kBlockSize;
 
 template <int kElemBytes>
 struct DecodeShape {
@@ -71,6 +72,8 @@ struct DecodeArgs {
   int32_t max_blocks;
   const int32_t* context_lens;
   int32_t batch, num_q_heads, num_kv_heads, group, head_chunks;
+  FastDiv bdiv;       // block size (bdiv.d) and division by it
+  int32_t bshift;     // log2(block size) when a chunk spans several blocks
   float scale_log2;
   int32_t split_tokens, nsplit;
   uint8_t* out;
@@ -103,7 +106,11 @@ __device__ __forceinline__ void unpack(const u32x4& w, float* f) {
   }
 }
 
-template <int kElemBytes, int kHeads, bool kFused>
+// kSmall: blocks shorter than a chunk (16 or 32 tokens, a power of two): each
+// 1 KiB load of a chunk still lies in one block, but consecutive loads of a
+// chunk may lie in different blocks, so each load gets its own block lookup.
+// Otherwise a chunk lies in one block and one lookup serves all its loads.
+template <int kElemBytes, int kHeads, bool kFused, bool kSmall>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   using S = DecodeShape<kElemBytes>;
   constexpr int kVec = S::kVec;
@@ -147,8 +154,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
                                              (int64_t)g * S::kRowBytes + col_ * 16);
       const int s_last = n > 0 ? (n - 1) / a.split_tokens : 0;
       if (hc == 0 && s == s_last && lane < kCPR) {
-        const int64_t off = (((int64_t)(slot_new / kBlockSize) * a.num_kv_heads + g) * kBlockSize +
-                             slot_new % kBlockSize) * S::kRowBytes + lane * 16;
+        const uint32_t p = a.bdiv.div((uint32_t)slot_new);
+        const int64_t off = (((int64_t)p * a.num_kv_heads + g) * a.bdiv.d +
+                             (slot_new - p * a.bdiv.d)) * S::kRowBytes + lane * 16;
         *reinterpret_cast<u32x4*>(a.k_cache_w + off) = knew;
         *reinterpret_cast<u32x4*>(a.v_cache_w + off) = vnew;
       }
@@ -189,23 +197,31 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const int t_row = lane % kTok;
 
   // Block-table entries of this split, one per lane, loaded once: a split
-  // spans at most 64 blocks (the plan keeps split_tokens <= 64 * 256 and a
-  // multiple of 256 above 256), so the per-chunk lookup is a readlane and
-  // never a load + wait inside the pipelined loop.
-  const int tab_base = start / kBlockSize;
+  // spans at most 64 blocks (the plan bounds split_tokens by the block
+  // size), so the per-chunk lookup is a readlane and never a load + wait
+  // inside the pipelined loop.
+  const uint32_t bs = a.bdiv.d;
+  const int tab_base = (int)a.bdiv.div((uint32_t)start);
   const int tab_idx = tab_base + lane;
-  const int tab = tab_idx < (end + kBlockSize - 1) / kBlockSize ? table[tab_idx] : 0;
+  const int tab = tab_idx < (int)a.bdiv.div((uint32_t)(end + bs - 1)) ? table[tab_idx] : 0;
   // Byte offset of the (block, kv head g) rows starting at key c0.
   auto chunk_base = [&](int c0) -> int64_t {
-    const int64_t blk = __builtin_amdgcn_readlane(tab, c0 / kBlockSize - tab_base);
-    return ((blk * a.num_kv_heads + g) * kBlockSize + (c0 % kBlockSize)) * S::kRowBytes;
+    const uint32_t q = kSmall ? (uint32_t)c0 >> a.bshift : a.bdiv.div((uint32_t)c0);
+    const int64_t blk = __builtin_amdgcn_readlane(tab, (int)q - tab_base);
+    return ((blk * a.num_kv_heads + g) * bs + (c0 - q * bs)) * S::kRowBytes;
+  };
+  // Byte offset of load i of the chunk at c0 (kRowsPerLoad rows, 1 KiB).
+  auto load_base = [&](int64_t cbase, int c0, int i) -> int64_t {
+    if constexpr (kSmall) return chunk_base(c0 + i * S::kRowsPerLoad);
+    else return cbase + i * 1024;
   };
   // position whose K/V come from the fused store's input (-1: none here)
   int p_new = -1;
   if (slot_new >= 0 && n - 1 >= start && n - 1 < end) {
     const int pos = n - 1;
-    const int blk = __builtin_amdgcn_readlane(tab, pos / kBlockSize - tab_base);
-    if (slot_new == blk * kBlockSize + pos % kBlockSize) p_new = pos;
+    const uint32_t q = a.bdiv.div((uint32_t)pos);
+    const int blk = __builtin_amdgcn_readlane(tab, (int)q - tab_base);
+    if (slot_new == blk * (int)bs + (pos - (int)(q * bs))) p_new = pos;
   }
 
   // Software pipeline: the next chunk's K is loaded as soon as the current
@@ -216,16 +232,17 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   // wait for every outstanding load at the join).
   u32x4 kr[S::kLoads], vr[S::kLoads];
   {
-    const int64_t base = chunk_base(start);
+    const int64_t base = kSmall ? 0 : chunk_base(start);
 #pragma unroll
     for (int i = 0; i < S::kLoads; ++i)
-      kr[i] = stream_load(a.k_cache + base + i * 1024 + lane * 16);
+      kr[i] = stream_load(a.k_cache + load_base(base, start, i) + lane * 16);
 #pragma unroll
     for (int i = 0; i < S::kLoads; ++i)
-      vr[i] = stream_load(a.v_cache + base + i * 1024 + lane * 16);
+      vr[i] = stream_load(a.v_cache + load_base(base, start, i) + lane * 16);
   }
 
   auto chunk = [&](int c0, auto prefetch_tag, int64_t next_base) {
+    const int c_next = c0 + kTok;
     constexpr bool kPrefetch = decltype(prefetch_tag)::value;
     __syncthreads();  // one wavefront: orders the previous chunk's LDS reads
 #pragma unroll
@@ -241,7 +258,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     if constexpr (kPrefetch) {
 #pragma unroll
       for (int i = 0; i < S::kLoads; ++i)
-        kr[i] = stream_load(a.k_cache + next_base + i * 1024 + lane * 16);
+        kr[i] = stream_load(a.k_cache + load_base(next_base, c_next, i) + lane * 16);
     }
 
     const int nvalid = min(kTok, end - c0);
@@ -319,12 +336,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     if constexpr (kPrefetch) {
 #pragma unroll
       for (int i = 0; i < S::kLoads; ++i)
-        vr[i] = stream_load(a.v_cache + next_base + i * 1024 + lane * 16);
+        vr[i] = stream_load(a.v_cache + load_base(next_base, c_next, i) + lane * 16);
     }
   };
 
   int c0 = start;
-  for (; c0 + kTok < end; c0 += kTok) chunk(c0, TrueTag{}, chunk_base(c0 + kTok));
+  for (; c0 + kTok < end; c0 += kTok) chunk(c0, TrueTag{}, kSmall ? 0 : chunk_base(c0 + kTok));
   chunk(c0, FalseTag{}, 0);
 
   // sum the token groups (lanes col, col + kCPR, ...) and the per-lane l
@@ -445,14 +462,22 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   }
 }
 
+template <int kElemBytes, int kHeads, bool kSmall>
+void launch_split_b(const DecodeArgs& args, unsigned grid, hipStream_t stream) {
+  if (args.k_new)
+    hipLaunchKernelGGL((decode_split_kernel<kElemBytes, kHeads, true, kSmall>), dim3(grid),
+                       dim3(64), 0, stream, args);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<kElemBytes, kHeads, false, kSmall>), dim3(grid),
+                       dim3(64), 0, stream, args);
+}
+
 template <int kElemBytes, int kHeads>
 void launch_split(const DecodeArgs& args, unsigned grid, hipStream_t stream) {
-  if (args.k_new)
-    hipLaunchKernelGGL((decode_split_kernel<kElemBytes, kHeads, true>), dim3(grid), dim3(64), 0,
-                       stream, args);
+  if ((int)args.bdiv.d < DecodeShape<kElemBytes>::kTokens)
+    launch_split_b<kElemBytes, kHeads, true>(args, grid, stream);
   else
-    hipLaunchKernelGGL((decode_split_kernel<kElemBytes, kHeads, false>), dim3(grid), dim3(64), 0,
-                       stream, args);
+    launch_split_b<kElemBytes, kHeads, false>(args, grid, stream);
 }
 
 template <int kElemBytes>
@@ -474,7 +499,7 @@ int decode_heads_per_wg(int group) {
 }
 
 bool plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_context_len,
-                 int num_splits, DecodePlan* plan) {
+                 int num_splits, int block_size, DecodePlan* plan) {
   const int group = num_q_heads / num_kv_heads;
   const int hpw = decode_heads_per_wg(group);
   if (hpw == 0) return false;
@@ -492,11 +517,16 @@ bool plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_context_l
   if (want < 1) want = 1;
   if (want > max_chunks) want = max_chunks;
   const int per = max_context_len > 0 ? (int)((max_context_len + want - 1) / want) : 64;
-  // Splits of up to 256 keys are multiples of 64 (a 64-key chunk never
-  // crosses a block); longer splits are whole blocks, at most 64 of them, so
-  // the split kernel can hold a split's block-table entries in one register.
-  int split = per <= kBlockSize ? ((per + 63) / 64) * 64 : ((per + kBlockSize - 1) / kBlockSize) * kBlockSize;
-  if (split > kMaxSplitTokens) split = kMaxSplitTokens;
+  // Splits of up to 256 keys are multiples of 64 (a chunk starts on a
+  // multiple of 64 and so never crosses a block of 64 k tokens); longer
+  // splits are multiples of 256.  A split's block-table entries must fit one
+  // register (64 lanes): a split aligned to the blocks spans split / B of
+  // them, an unaligned one up to split / B + 2.
+  int split = per <= 256 ? ((per + 63) / 64) * 64 : ((per + 255) / 256) * 256;
+  const int gran = split <= 256 ? 64 : 256;
+  const int64_t cap_tokens = (gran % block_size == 0 ? 64 : 62) * (int64_t)block_size;
+  const int cap = (int)std::min<int64_t>(cap_tokens / gran * gran, 1 << 30);
+  if (split > cap) split = cap;
   plan->split_tokens = split;
   plan->nsplit = max_context_len > 0 ? (max_context_len + plan->split_tokens - 1) / plan->split_tokens : 1;
   if (plan->nsplit > 1) {
@@ -521,6 +551,9 @@ static DecodeArgs decode_args(int elem_bytes, const DecodePlan& plan, const Deco
   a.num_kv_heads = l.num_kv_heads;
   a.group = plan.group;
   a.head_chunks = plan.head_chunks;
+  a.bdiv = FastDiv((uint32_t)l.block_size);
+  a.bshift = 0;
+  while ((1 << a.bshift) < l.block_size) ++a.bshift;
   a.scale_log2 = l.scale * kLog2e;
   a.split_tokens = plan.split_tokens;
   a.nsplit = plan.nsplit;

@@ -21,7 +21,7 @@ template <int kElemBytes>
 __global__ __launch_bounds__(256) void kv_store_kernel(
     const uint8_t* __restrict__ k, int64_t k_stride_bytes, const uint8_t* __restrict__ v,
     int64_t v_stride_bytes, uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
-    const int32_t* __restrict__ slots, int64_t num_chunks, int num_kv_heads) {
+    const int32_t* __restrict__ slots, int64_t num_chunks, int num_kv_heads, FastDiv bdiv) {
   constexpr int kRowBytes = kHeadDim * kElemBytes;
   constexpr int kChunksPerRow = kRowBytes / 16;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -32,9 +32,9 @@ __global__ __launch_bounds__(256) void kv_store_kernel(
     const int g = (int)(row % num_kv_heads);
     const int32_t s = slots[t];
     if (s < 0) continue;
-    const int64_t p = s / kBlockSize;
-    const int o = s % kBlockSize;
-    const int64_t dst = ((p * num_kv_heads + g) * kBlockSize + o) * kRowBytes + c * 16;
+    const uint32_t p = bdiv.div((uint32_t)s);  // block, row of the slot
+    const int o = s - (int)(p * bdiv.d);
+    const int64_t dst = (((int64_t)p * num_kv_heads + g) * bdiv.d + o) * kRowBytes + c * 16;
     const int64_t src_off = (int64_t)g * kRowBytes + c * 16;
     const u32x4 kv = *reinterpret_cast<const u32x4*>(k + t * k_stride_bytes + src_off);
     const u32x4 vv = *reinterpret_cast<const u32x4*>(v + t * v_stride_bytes + src_off);
@@ -45,7 +45,8 @@ __global__ __launch_bounds__(256) void kv_store_kernel(
 
 hipError_t launch_kv_store(int elem_bytes, const void* k, int64_t k_stride, const void* v,
                            int64_t v_stride, void* k_cache, void* v_cache, const int32_t* slots,
-                           int num_tokens, int num_kv_heads, hipStream_t stream) {
+                           int num_tokens, int num_kv_heads, int block_size,
+                           hipStream_t stream) {
   const int64_t chunks_per_row = (int64_t)kHeadDim * elem_bytes / 16;
   const int64_t num_chunks = (int64_t)num_tokens * num_kv_heads * chunks_per_row;
   const int threads = 256;
@@ -53,14 +54,15 @@ hipError_t launch_kv_store(int elem_bytes, const void* k, int64_t k_stride, cons
   const int64_t max_blocks = 256 * 64;  // grid-stride beyond this
   if (blocks > max_blocks) blocks = max_blocks;
   const int64_t ksb = k_stride * elem_bytes, vsb = v_stride * elem_bytes;
+  const FastDiv bdiv((uint32_t)block_size);
   if (elem_bytes == 2) {
     hipLaunchKernelGGL(kv_store_kernel<2>, dim3((unsigned)blocks), dim3(threads), 0, stream,
                        (const uint8_t*)k, ksb, (const uint8_t*)v, vsb, (uint8_t*)k_cache,
-                       (uint8_t*)v_cache, slots, num_chunks, num_kv_heads);
+                       (uint8_t*)v_cache, slots, num_chunks, num_kv_heads, bdiv);
   } else {
     hipLaunchKernelGGL(kv_store_kernel<4>, dim3((unsigned)blocks), dim3(threads), 0, stream,
                        (const uint8_t*)k, ksb, (const uint8_t*)v, vsb, (uint8_t*)k_cache,
-                       (uint8_t*)v_cache, slots, num_chunks, num_kv_heads);
+                       (uint8_t*)v_cache, slots, num_chunks, num_kv_heads, bdiv);
   }
   return hipGetLastError();
 }

@@ -7,13 +7,44 @@
 
 namespace pkv {
 
-constexpr int kHeadDim = 128;    // head_dim supported by the kernels
-constexpr int kBlockSize = 256;  // tokens per KV block
+constexpr int kHeadDim = 128;      // head_dim supported by the kernels
+constexpr int kBlockSize = 256;    // the pages' tokens per KV block
+constexpr int kMaxBlockSize = 4096;
+
+// Block sizes the kernels take: 16 and 32 (a 64-token tile spans several
+// blocks; each 16-row quarter lies in one) and every multiple of 64 up to
+// kMaxBlockSize (a 64-token tile lies in one block), which includes all
+// multiples of 256.
+inline bool block_size_supported(int b) {
+  return b == 16 || b == 32 || (b > 0 && b % 64 == 0 && b <= kMaxBlockSize);
+}
+
+// Division of n in [0, 2^32) by a divisor fixed at launch, by multiplication
+// (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994, the unsigned round-up method): with
+// l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1,
+// n / d = (t + ((n - t) >> min(l, 1))) >> max(l - 1, 0), t = mulhi(m, n).
+struct FastDiv {
+  uint32_t d = 1, m = 1, s1 = 0, s2 = 0;
+  FastDiv() = default;
+  explicit FastDiv(uint32_t div) : d(div) {
+    uint32_t l = 0;
+    while (l < 32 && (1ull << l) < div) ++l;
+    m = (uint32_t)(((1ull << 32) * ((1ull << l) - div)) / div + 1);
+    s1 = l < 1 ? l : 1;
+    s2 = l > 1 ? l - 1 : 0;
+  }
+  __host__ __device__ __forceinline__ uint32_t div(uint32_t n) const {
+    const uint32_t t = (uint32_t)(((uint64_t)m * n) >> 32);
+    return (t + ((n - t) >> s1)) >> s2;
+  }
+};
 
 // ---- slot scatter -------------------------------------------------------
 hipError_t launch_kv_store(int elem_bytes, const void* k, int64_t k_stride, const void* v,
                            int64_t v_stride, void* k_cache, void* v_cache, const int32_t* slots,
-                           int num_tokens, int num_kv_heads, hipStream_t stream);
+                           int num_tokens, int num_kv_heads, int block_size,
+                           hipStream_t stream);
 
 // ---- paged decode -------------------------------------------------------
 // Query heads of one GQA group handled by one decode workgroup.
@@ -30,7 +61,7 @@ struct DecodePlan {
 
 // Returns false if the group size is not supported.
 bool plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_context_len,
-                 int num_splits, DecodePlan* plan);
+                 int num_splits, int block_size, DecodePlan* plan);
 
 struct DecodeLaunch {
   const void* q;
@@ -41,6 +72,7 @@ struct DecodeLaunch {
   int32_t max_blocks;
   const int32_t* context_lens;
   int32_t batch, num_q_heads, num_kv_heads;
+  int32_t block_size = kBlockSize;  // block_size_supported()
   float scale;
   void* out;
   float* workspace;
@@ -74,6 +106,7 @@ struct PrefillLaunch {
   const int32_t* block_tables;
   int32_t max_blocks;
   int32_t batch, num_q_heads, num_kv_heads;
+  int32_t block_size = kBlockSize;  // block_size_supported()
   float scale;
   void* out;
   void* workspace;  // prefill_workspace_bytes(), zero on entry, zero on exit

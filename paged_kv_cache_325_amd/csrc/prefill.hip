@@ -84,6 +84,7 @@ struct PrefillArgs {
   const uint16_t* k_rows;
   const uint16_t* v_rows;
   int64_t k_row_stride, v_row_stride;  // elements between key rows
+  FastDiv bdiv;  // cache block size (bdiv.d) and division by it
   int32_t num_items;   // work items: (query tile, sequence, kv head, head chunk)
   int32_t num_queues;  // work queues (one per XCD when the grid allows)
   int32_t* counters;   // [kMaxQueues] queue heads, then the exit count
@@ -112,11 +113,15 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 __device__ __forceinline__ int k_pos(int key, int c) { return c ^ (key & 15); }
 __device__ __forceinline__ int v_pos(int key, int c) { return c ^ ((key & 7) << 1); }
 
-// Copy one 64-key tile (K or V, rows k0 .. k0+63 of a (block, kv head),
-// `rsrc` addressing it) into LDS: each of the 4 group-A waves moves 16 keys,
-// 1 KiB per instruction.  The per-lane byte offsets depend only on the lane
-// and wave, so they are computed once (tile_offsets) and a new tile only
-// changes the scalar buffer base.
+// Copy one 64-key tile (K or V) into LDS: each of the 4 group-A waves moves
+// 16 keys, 1 KiB per instruction.  The per-lane byte offsets depend only on
+// the lane and wave, so they are computed once (tile_offsets) and a new tile
+// only changes the scalar buffer base.  With cache blocks of a multiple of 64
+// tokens a tile lies in one block and one resource (base row k0) serves the
+// 4 waves (`wave` = the wave's index in its group).  With blocks of 16 or 32
+// tokens a tile spans several blocks; each wave's 16 rows still lie in one,
+// so each wave uses its own resource based at its first row (`wave` = 0).
+// The swizzle uses key & 15, the same either way.
 template <bool kIsV>
 __device__ __forceinline__ void tile_offsets(uint32_t (&voff)[4], int wave, int lane,
                                              uint32_t row_bytes) {
@@ -167,6 +172,11 @@ __device__ __forceinline__ void phase_barrier() {
 
 // One work item: query tile r (counted from the end) of sequence b, kv head
 // g, head chunk hc, on 8 waves in two groups of 4 (see the kernel).
+// kBlock: the cache block size when it is fixed at compile time (256, the
+// pages' size: divisions become shifts), 0 for any other multiple of 64
+// (division by multiplication), -1 for blocks of 16 or 32 tokens (see
+// tile_offsets).
+template <int kBlock>
 __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4 (*kbuf)[kKT * 16],
                                              u32x4 (*vbuf)[kKT * 16]) {
   const int tid = threadIdx.x;
@@ -226,7 +236,14 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4
   // every vector memory access in flight, including the copies of the
   // previous tiles.
   const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
-  const int nblk = a.cu_k ? 0 : (wg_kend + kBlockSize - 1) / kBlockSize;
+  constexpr bool kSmall = kBlock < 0;
+  const uint32_t bs = kBlock > 0 ? (uint32_t)kBlock : a.bdiv.d;
+  auto block_of = [&](uint32_t key) -> uint32_t {
+    if constexpr (kBlock > 0) return key / (uint32_t)kBlock;
+    else if constexpr (kSmall) return key >> (bs == 16 ? 4 : 5);
+    else return a.bdiv.div(key);
+  };
+  const int nblk = a.cu_k ? 0 : (int)block_of((uint32_t)(wg_kend + bs - 1));
   const int32_t tab0 = lane < nblk ? table[lane] : 0;
   const int32_t tab1 = lane + 64 < nblk ? table[lane + 64] : 0;
   auto block_at = [&](int i) -> int64_t {  // i uniform
@@ -239,24 +256,56 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4
   const uint32_t k_row_bytes = a.cu_k ? (uint32_t)(a.k_row_stride * 2) : kHeadDim * 2;
   const uint32_t v_row_bytes = a.cu_k ? (uint32_t)(a.v_row_stride * 2) : kHeadDim * 2;
   uint32_t k_off[4], v_off[4];
-  tile_offsets<false>(k_off, wave & (kGroupWaves - 1), lane, k_row_bytes);
-  tile_offsets<true>(v_off, wave & (kGroupWaves - 1), lane, v_row_bytes);
-  auto issue_copy = [&](int t) {  // group A only
+  const int gw = kSmall ? 0 : (wave & (kGroupWaves - 1));
+  tile_offsets<false>(k_off, gw, lane, k_row_bytes);
+  tile_offsets<true>(v_off, gw, lane, v_row_bytes);
+  // kBlock == 0: the copies run over the tiles in order, so the tile's
+  // (block index, row in block) advances by one tile per call instead of
+  // being divided out
+  uint32_t cp_blk = 0, cp_row = 0;
+  auto issue_copy = [&](int t) {  // group A only, t = 0, 1, 2, ... in order
     const int k0 = t * kKT;
     const int nvalid = min(kKT, n_k - k0);
     const uint16_t *kb, *vb;
-    if (a.cu_k) {
-      kb = a.k_rows + (int64_t)(k_begin + k0) * a.k_row_stride + g * kHeadDim;
-      vb = a.v_rows + (int64_t)(k_begin + k0) * a.v_row_stride + g * kHeadDim;
+    int nbytes_k, nbytes_v;
+    if constexpr (!kSmall) {
+      if (a.cu_k) {
+        kb = a.k_rows + (int64_t)(k_begin + k0) * a.k_row_stride + g * kHeadDim;
+        vb = a.v_rows + (int64_t)(k_begin + k0) * a.v_row_stride + g * kHeadDim;
+      } else {
+        uint32_t qb, row;
+        if constexpr (kBlock > 0) {
+          qb = block_of((uint32_t)k0);
+          row = k0 - qb * bs;
+        } else {
+          qb = cp_blk;
+          row = cp_row;
+          cp_row += kKT;
+          if (cp_row == bs) cp_row = 0, ++cp_blk;
+        }
+        const int64_t blk = block_at((int)qb);
+        const int64_t base = ((blk * a.num_kv_heads + g) * bs + row) * kHeadDim;
+        kb = a.k_cache + base;
+        vb = a.v_cache + base;
+      }
+      nbytes_k = nvalid * (int)k_row_bytes;
+      nbytes_v = nvalid * (int)v_row_bytes;
     } else {
-      const int64_t blk = block_at(k0 / kBlockSize);
-      const int64_t base = ((blk * a.num_kv_heads + g) * kBlockSize + (k0 % kBlockSize)) * kHeadDim;
+      // this wave's 16 keys kw .. kw+15 lie in one block; keys at or past
+      // wg_kend are seen by no query of the workgroup, arrive as zeros
+      // (outside the resource) and need no (possibly unloaded) table entry
+      const int kw = k0 + __builtin_amdgcn_readfirstlane((wave & (kGroupWaves - 1)) * 16);
+      const int nv = max(0, min(16, wg_kend - kw));
+      const uint32_t qb = nv > 0 ? block_of((uint32_t)kw) : 0u;
+      const int64_t blk = nv > 0 ? block_at((int)qb) : 0;
+      const int64_t base = ((blk * a.num_kv_heads + g) * bs + (kw - qb * bs)) * kHeadDim;
       kb = a.k_cache + base;
       vb = a.v_cache + base;
+      nbytes_k = nbytes_v = nv * kHeadDim * 2;
     }
     const int slot = t % kSlots;
-    tile_to_lds(tile_rsrc(kb, nvalid * (int)k_row_bytes), k_off, kbuf[slot], wave);
-    tile_to_lds(tile_rsrc(vb, nvalid * (int)v_row_bytes), v_off, vbuf[slot], wave);
+    tile_to_lds(tile_rsrc(kb, nbytes_k), k_off, kbuf[slot], wave);
+    tile_to_lds(tile_rsrc(vb, nbytes_v), v_off, vbuf[slot], wave);
   };
 
   // PV operand reads (ds_read_b64_tr_b16): in each 16-lane group, lane
@@ -459,6 +508,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4
 // however unequal the items are (the hardware dispatcher leaves slots idle
 // when workgroup lengths vary).  The last workgroup to leave resets the
 // counters, so the workspace is zero again when the kernel ends.
+template <int kBlock>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
   // K and V tiles, 4 slots each (128 KiB).
   __shared__ u32x4 kbuf[kSlots][kKT * 16];
@@ -487,7 +537,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     // item's indices (and the block-table entries) in scalar registers
     const int id = __builtin_amdgcn_readfirstlane(next_item[it & 1]);
     if (id < 0) break;
-    prefill_item(a, id, kbuf, vbuf);
+    prefill_item<kBlock>(a, id, kbuf, vbuf);
     // Alternating slots: thread 0 cannot rewrite a slot before every thread
     // has passed the barrier below, i.e. has read it.
     if (threadIdx.x == 0) next_item[(it + 1) & 1] = pull();
@@ -563,7 +613,14 @@ hipError_t launch_prefill(const PrefillLaunch& l, hipStream_t stream) {
   a.v_rows = (const uint16_t*)l.v_rows;
   a.k_row_stride = l.k_row_stride;
   a.v_row_stride = l.v_row_stride;
-  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  a.bdiv = FastDiv((uint32_t)l.block_size);
+  if (a.cu_k || l.block_size == kBlockSize)  // contiguous keys use no block
+    hipLaunchKernelGGL(prefill_kernel<kBlockSize>, dim3((unsigned)grid), dim3(kThreads), 0,
+                       stream, a);
+  else if (l.block_size < kKT)  // 16 or 32
+    hipLaunchKernelGGL(prefill_kernel<-1>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(prefill_kernel<0>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -65,7 +65,8 @@ def test_kv_store_errors():
     assert _store(slots=None) == INVALID
     assert _store(dtype=5) == INVALID
     assert _store(d=64) == UNSUPPORTED
-    assert _store(bs=16) == UNSUPPORTED
+    for bs in (8, 48, 100, 4160, 8192):  # supported: 16, 32, multiples of 64 up to 4096
+        assert _store(bs=bs) == UNSUPPORTED, bs
     assert _store(hkv=0) == INVALID
     assert _store(ks=100) == INVALID  # smaller than a row
     assert _store(ks=1028) == INVALID  # rows not 16-byte aligned
@@ -120,7 +121,8 @@ def test_decode_errors():
     assert _decode(hq=24) == UNSUPPORTED  # group of 3
     assert _decode(hq=0) == INVALID
     assert _decode(d=256) == UNSUPPORTED
-    assert _decode(bs=128) == UNSUPPORTED
+    assert _decode(bs=48) == UNSUPPORTED
+    assert _decode(bs=128) == INVALID  # supported, but 4096 > 16 table columns * 128
     assert _decode(maxctx=16 * 256 + 1) == INVALID  # beyond the table
     assert _decode(q=None) == INVALID
     assert _decode(out=FAKE + 8) == INVALID
@@ -149,6 +151,14 @@ def test_decode_split_plan():
     assert pkv.pkv_paged_decode_split_tokens(4, 16, 8, 128, 4096, 256, 1) >= 4096
     assert pkv.pkv_paged_decode_split_tokens(4, 16, 8, 128, 32768, 256, 1) == 16384
     assert pkv.pkv_paged_decode_workspace_bytes(4, 16, 8, 64, 4096, 256, 0) == 0  # unsupported
+    assert pkv.pkv_paged_decode_workspace_bytes(4, 16, 8, 128, 4096, 48, 0) == 0  # unsupported
+    # a split's block-table entries fit one register: at most 64 blocks when
+    # splits are aligned to the blocks, 62 otherwise
+    assert pkv.pkv_paged_decode_split_tokens(4, 16, 8, 128, 32768, 16, 1) == 1024
+    assert pkv.pkv_paged_decode_split_tokens(4, 16, 8, 128, 32768, 32, 1) == 2048
+    assert pkv.pkv_paged_decode_split_tokens(4, 16, 8, 128, 32768, 64, 1) == 4096
+    assert pkv.pkv_paged_decode_split_tokens(4, 16, 8, 128, 65536, 512, 1) == 31744
+    assert pkv.pkv_paged_decode_split_tokens(4, 16, 8, 128, 65536, 1024, 1) == 63488
 
 
 def _prefill(**kw):

@@ -1,0 +1,160 @@
+"""Block sizes other than 256 (16, 32 and multiples of 64 up to 4096, which
+include every multiple of 256): store, decode, the fused decode step and the
+paged prefill against the CPU oracle on the small parity cases re-drawn at
+each block size, and a layout invariant -- the same logical K/V laid out in
+blocks of another size give bitwise the outputs of the 256-token layout."""
+
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_325_amd as pkv
+from tests.gpu_helpers import announce, assert_close, attend, check_inputs, store, to_device
+from tests.oracle_helpers import expected, stored_bits
+from workloads import bits_view, build, config, small_specs
+
+pytestmark = pytest.mark.gpu
+
+SIZES = [16, 32, 64, 128, 512, 768, 1024]
+
+
+def at_block_size(spec, B):
+    """The spec with blocks of B tokens; shared prefixes keep (at most) the
+    same number of tokens, rounded down to whole blocks."""
+    shared = None
+    if spec.shared_blocks:
+        shared = [min(s * 256 // B, (c - n) // B) for s, c, n in
+                  zip(spec.shared_blocks, spec.context_lens, spec.new_tokens)]
+    return dataclasses.replace(spec, name=f"{spec.name}-B{B}", block_size=B,
+                               shared_blocks=shared, seed=spec.seed + B)
+
+
+CASES = [(s, B) for B in SIZES for s in small_specs()
+         if s.name in ("dec-bf16-g2-ragged", "dec-fp32-g2", "dec-bf16-shared", "dec-bf16-g8",
+                       "dec-bf16-empty-ctx", "pre-bf16-g4", "pre-bf16-g2", "pre-bf16-g8")]
+
+
+@pytest.mark.parametrize("spec,B", CASES, ids=[f"{s.name}-B{B}" for s, B in CASES])
+def test_block_size_against_oracle(spec, B):
+    w = build(at_block_size(spec, B))
+    d = to_device(w)
+    check_inputs(d)
+    announce(f"block size {B}: {w.spec.name}")
+    store(d)
+    out = attend(d)
+    torch.cuda.synchronize()
+    kcb, vcb = stored_bits(w)
+    assert np.array_equal(bits_view(d.k_cache.cpu()), kcb)
+    assert np.array_equal(bits_view(d.v_cache.cpu()), vcb)
+    assert_close(out.to(torch.float64).cpu().numpy(), expected(w), w.spec.name)
+    if w.spec.mode == "decode":
+        for splits in (1, 3):
+            o2 = attend(d, num_splits=splits)
+            torch.cuda.synchronize()
+            assert_close(o2.to(torch.float64).cpu().numpy(), expected(w),
+                         f"{w.spec.name} splits={splits}")
+
+
+@pytest.mark.parametrize("B", [16, 32, 512])
+def test_fused_step_at_block_size(B):
+    spec = [s for s in small_specs() if s.name == "dec-bf16-g2-ragged"][0]
+    w = build(at_block_size(spec, B))
+    a, b = to_device(w), to_device(w)
+    check_inputs(a)
+    announce(f"fused step at block size {B}")
+    store(a)
+    ref_out = attend(a)
+    out = pkv.pkv_paged_decode_step(b.q, b.k, b.v, b.slot_mapping, b.k_cache, b.v_cache,
+                                    b.block_tables, b.context_lens, w.max_context_len, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+    assert torch.equal(a.k_cache.view(torch.int16), b.k_cache.view(torch.int16))
+    assert torch.equal(a.v_cache.view(torch.int16), b.v_cache.view(torch.int16))
+
+
+def _relayout(w, B2, seed):
+    """The post-store caches of w re-laid out in shuffled blocks of B2 tokens
+    (logical rows of each sequence copied out; cells outside every context
+    stay NaN), with matching tables."""
+    kcb, vcb = stored_bits(w)
+    B, batch = w.block_size, w.batch
+    nb2 = [-(-int(c) // B2) for c in w.context_lens]
+    pool = max(1, sum(nb2))
+    perm = np.random.default_rng(seed).permutation(pool)
+    nan = np.uint16(0x7FC1)
+    k2 = np.full((pool, w.num_kv_heads, B2, w.head_dim), nan, np.uint16)
+    v2 = np.full_like(k2, nan)
+    tables = np.full((batch, max(1, max(nb2))), -1, np.int32)
+    cur = 0
+    for b in range(batch):
+        n = int(w.context_lens[b])
+        tables[b, :nb2[b]] = perm[cur:cur + nb2[b]]
+        cur += nb2[b]
+        pos = np.arange(n)
+        src_blk = w.block_tables[b, pos // B].astype(np.int64)
+        dst_blk = tables[b, pos // B2].astype(np.int64)
+        k2[dst_blk, :, pos % B2] = kcb[src_blk, :, pos % B]
+        v2[dst_blk, :, pos % B2] = vcb[src_blk, :, pos % B]
+    return k2, v2, tables
+
+
+def _t(bits):
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+@pytest.mark.parametrize("B2", [16, 32, 64, 512, 1024])
+@pytest.mark.parametrize("name", ["dec-bf16-g2-ragged", "dec-bf16-g4-long", "pre-bf16-g4",
+                                  "pre-bf16-g2"])
+def test_layout_invariance_bitwise(name, B2):
+    spec = [s for s in small_specs() if s.name == name][0]
+    w = build(spec)
+    d = to_device(w)
+    check_inputs(d)
+    announce(f"layout invariance {name} at block size {B2}")
+    store(d)
+    ref_out = attend(d)
+    k2, v2, tables = _relayout(w, B2, 77 + B2)
+    kc, vc = _t(k2), _t(v2)
+    tab = torch.from_numpy(tables).cuda()
+    ctx = d.context_lens
+    if spec.mode == "decode":
+        out = pkv.pkv_paged_decode(d.q, kc, vc, tab, ctx, w.max_context_len, w.scale)
+    else:
+        out = pkv.pkv_paged_prefill_varlen(d.q, kc, vc, d.cu_seqlens_q, w.max_seqlen_q, ctx,
+                                           w.max_context_len, tab, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+
+
+@pytest.mark.parametrize("B2", [16, 1024])
+@pytest.mark.parametrize("index", [2, 3])
+def test_full_size_layout_invariance_bitwise(index, B2):
+    # the 64-sequence decode and the prefill workload (checked against the
+    # oracle in their 256-token layout by the parity tests) re-laid out in
+    # blocks of 16 and 1024 tokens: outputs bitwise unchanged
+    w = config(index)
+    d = to_device(w)
+    check_inputs(d)
+    announce(f"full-size layout invariance, workload {index}, block size {B2}")
+    store(d)
+    ref_out = attend(d)
+    k2, v2, tables = _relayout(w, B2, 99 + B2)
+    kc, vc = _t(k2), _t(v2)
+    del k2, v2
+    tab = torch.from_numpy(tables).cuda()
+    if w.spec.mode == "decode":
+        # the same split plan (the cap binds at neither block size here)
+        S = pkv.pkv_paged_decode_split_tokens(w.batch, w.num_q_heads, w.num_kv_heads, 128,
+                                              w.max_context_len, 256, 0)
+        assert S == pkv.pkv_paged_decode_split_tokens(w.batch, w.num_q_heads, w.num_kv_heads,
+                                                      128, w.max_context_len, B2, 0)
+        out = pkv.pkv_paged_decode(d.q, kc, vc, tab, d.context_lens, w.max_context_len, w.scale)
+    else:
+        out = pkv.pkv_paged_prefill_varlen(d.q, kc, vc, d.cu_seqlens_q, w.max_seqlen_q,
+                                           d.context_lens, w.max_context_len, tab, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
