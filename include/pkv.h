@@ -32,7 +32,13 @@
  * element (p, g, o, d) is at ((p * num_kv_heads + g) * block_size + o) *
  * head_dim + d.  Physical slot s means block s / block_size, row
  * s % block_size.  This keeps the rows of one (block, kv head) contiguous.
- * block_size must be 256 and head_dim 128.
+ * head_dim must be 128.  block_size: 256 is the pages' size ("Kern-
+ * Designentscheidungen" item 1) and the tuned one; also taken are 16 and 32
+ * (vLLM's small pages) and every multiple of 64 up to 4096, which includes
+ * all multiples of 256 (the size the architecture page's configuration
+ * allows).  Outputs do not depend on the block size: the same logical K/V in
+ * blocks of any supported size give bitwise the same results (when the
+ * decode split plan is the same, see pkv_paged_decode_split_tokens).
  *
  * GQA: query head h reads kv head h / (num_q_heads / num_kv_heads).
  * Attention: out = sum_j softmax_j(scale * q . k_j) v_j over the visible keys,
@@ -45,7 +51,8 @@
  *                        num_q_heads % num_kv_heads != 0, misalignment,
  *                        max_context_len > max_blocks_per_seq * block_size,
  *                        causal != 1;
- *   PKV_ERR_UNSUPPORTED  block_size != 256, head_dim != 128, a GQA group size
+ *   PKV_ERR_UNSUPPORTED  a block_size outside {16, 32, 64 k <= 4096},
+ *                        head_dim != 128, a GQA group size
  *                        not in {1, 2, 4, 8} and not a multiple of 8, fp32
  *                        prefill;
  *   PKV_ERR_WORKSPACE    decode workspace smaller than required;
@@ -119,8 +126,9 @@ size_t pkv_paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
 /*
  * pkv_paged_decode_split_tokens -- keys per split that pkv_paged_decode uses
  * with these arguments: a multiple of 64 up to 256, a multiple of 256 above,
- * never more than 16384 (so a requested split count is an upper bound only
- * up to that size); >= max_context_len means one split.  Returns 0 for
+ * never more than 64 blocks (62 when splits are not aligned to the blocks:
+ * 16384 at block_size 256; so a requested split count is an upper bound
+ * only up to that size); >= max_context_len means one split.  Returns 0 for
  * invalid or unsupported arguments.
  */
 int32_t pkv_paged_decode_split_tokens(int32_t batch, int32_t num_q_heads,
