@@ -254,11 +254,11 @@ def time_fused_step(d: Device, steps: int, warmup: int, torch):
 # changes, the figure no longer describes the kernel and is reported as null.
 TRAFFIC = {
     ("decode_split_kernel", "decode-bf16-b64-ctx512-4096-h16-8"): {
-        "bytes": 553428083, "source": "decode.hip",
-        "sha256": "84248992c6af5fc9ba6aa48e1583d07309286d2599f3bca2a67eb4f240776112"},
+        "bytes": 553428369, "source": "decode.hip",
+        "sha256": "2288387c273635bea6a602e3b031ecdced6a4175b008437883700f9a772d9bd0"},
     ("prefill_kernel", "prefill-bf16-8seq-L1024-4096-prefix512-h32-8"): {
-        "bytes": 1898145669, "source": "prefill.hip",
-        "sha256": "09b3f3c2a32cd60d5ca2345306c8fead9803aaba19b7e9ed0c8d5b919030be50"},
+        "bytes": 1894308396, "source": "prefill.hip",
+        "sha256": "63973562676983ef311518d3e863d73535cc73ba46f444f1e35dc948eb8ff45a"},
 }
 
 
