@@ -450,9 +450,10 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4
   // phase V(t) = softmax(t).  Group B runs one phase behind group A, and
   // every phase ends in a workgroup barrier, so while the waves of one group
   // issue MFMAs the waves of the other (on the same SIMDs) run the softmax.
-  // Group A copies tile t+2 during V(t) (slots rotate over 4 tiles: K(t) is
-  // last read by B in M(t), V(t) by B in M(t+1)); before the barrier that
-  // ends V(t) it waits for its copies of tile t+1.
+  // Group A copies tile t+2 at the start of V(t) (slots rotate over 4 tiles:
+  // K(t) is last read by B in M(t), V(t) by B in M(t+1), so the slot of tile
+  // t-2 is free once V(t-1) has ended); before the barrier that ends V(t) it
+  // waits for its copies of tile t+1.
   if (group_a) {
     if (ntiles > 0) issue_copy(0);
     if (ntiles > 1) {
@@ -468,14 +469,14 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4
     if (t >= 1 && t - 1 < my_tiles) pv(t - 1);
     if (t < my_tiles) scores(t);
     phase_barrier();
+    // copies are issued before the softmax: the next MFMA phase's first
+    // operand read waits for them (the compiler cannot tell their LDS slot
+    // from the one it reads), so they get the softmax's time to land
+    if (group_a && t + kAhead < ntiles) issue_copy(t + kAhead);
     if (t < my_tiles) softmax(t);
     if (group_a) {
-      if (t + kAhead < ntiles) {
-        issue_copy(t + kAhead);
-        wait_vmcnt<kCopyOps>();
-      } else {
-        wait_vmcnt<0>();
-      }
+      if (t + kAhead < ntiles) wait_vmcnt<kCopyOps>();
+      else wait_vmcnt<0>();
     }
     phase_barrier();
   }
