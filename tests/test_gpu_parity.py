@@ -259,6 +259,29 @@ def test_prefill_single_query_matches_decode():
     assert_close(outp.double().cpu().numpy(), expected(wp), "prefill vs oracle")
 
 
+def test_mixed_chunked_prefill_and_decode_batch():
+    # one varlen call holding decode rows (one query at the end of a long
+    # context), chunks of a prompt whose earlier chunks are cached (queries
+    # in the middle of the context), a fresh prompt and a chunk that ends on
+    # a block boundary: the batch a chunked-prefill scheduler mixes
+    ctx = [1500, 700, 257, 1024, 3000, 64, 512]
+    new = [1, 300, 257, 512, 1, 64, 1]
+    w = build(Spec("mixed", "prefill", "bf16", 16, 8, ctx, new, 778,
+                   share_group=[0, 0, -1, -1, 0, -1, -1], shared_blocks=[2, 1, 0, 0, 2, 0, 0]))
+    d, out = _run_step(w)
+    assert_close(out.double().cpu().numpy(), expected(w), "mixed batch")
+    # each decode row equals pkv_paged_decode of that sequence alone
+    rows = [int(w.cu_seqlens_q[b]) for b in range(w.batch) if new[b] == 1]
+    seqs = [b for b in range(w.batch) if new[b] == 1]
+    sel = torch.tensor(seqs, device=d.q.device)
+    q1 = d.q[torch.tensor(rows, device=d.q.device)].contiguous()
+    outd = pkv.pkv_paged_decode(q1, d.k_cache, d.v_cache, d.block_tables[sel].contiguous(),
+                                d.context_lens[sel].contiguous(), w.max_context_len, w.scale)
+    torch.cuda.synchronize()
+    assert_close(out[torch.tensor(rows, device=d.q.device)].double().cpu().numpy(),
+                 outd.double().cpu().numpy(), "decode rows of the mixed batch vs decode")
+
+
 @pytest.mark.parametrize("spec", [
     Spec("pre-tiny-1item", "prefill", "bf16", 4, 1, [40], [40], 801),
     Spec("pre-tiny-6items", "prefill", "bf16", 4, 1, [70, 20], [70, 20], 802),
