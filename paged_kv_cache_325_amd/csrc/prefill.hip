@@ -105,13 +105,16 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // K and V tiles live in LDS in their natural [64 keys][128 dims] bf16 order,
 // 256 bytes per key row, with the 16-byte chunks of row `key` permuted:
 //   K: chunk c at position c ^ (key & 15)
-//   V: chunk c at position c ^ (2 * (key & 7))   (32-byte blocks permuted)
-// so that the MFMA operand reads below hit distinct LDS banks.  Tiles are
+//   V: chunk c at position c ^ (4 * (key & 3))   (64-byte blocks permuted)
+// so that the MFMA operand reads below hit distinct LDS banks.  (For V the
+// transpose reads of one instruction cover 8 keys x 8 dim groups; with the
+// permutation the 32 lanes of each half wave address 32 distinct 8-byte
+// bank pairs -- rocprofv3 SQ_LDS_BANK_CONFLICT reads 0.)  Tiles are
 // copied global -> LDS by the direct-to-LDS load (no registers, no VALU):
 // lane l of a wave instruction lands at LDS base + 16 l, so each lane fetches
 // the global chunk that belongs at that position.
 __device__ __forceinline__ int k_pos(int key, int c) { return c ^ (key & 15); }
-__device__ __forceinline__ int v_pos(int key, int c) { return c ^ ((key & 7) << 1); }
+__device__ __forceinline__ int v_pos(int key, int c) { return c ^ ((key & 3) << 2); }
 
 // Copy one 64-key tile (K or V) into LDS: each of the 4 group-A waves moves
 // 16 keys, 1 KiB per instruction.  The per-lane byte offsets depend only on
