@@ -70,6 +70,34 @@ def test_decode_forced_splits(splits):
     assert_close(out.to(torch.float64).cpu().numpy(), expected(w), f"splits={splits}")
 
 
+def test_decode_more_than_64_splits():
+    # 100 requested splits of a 16 k context: splits of 192 keys, 86 of them,
+    # so the merge takes its loop over more than one group of 64 splits
+    w = build(Spec("dec-long-86", "decode", "bf16", 8, 2, [16384, 9000, 300], [1] * 3, 9201))
+    S = pkv.pkv_paged_decode_split_tokens(w.batch, 8, 2, 128, w.max_context_len, 256, 100)
+    assert S == 192 and -(-16384 // S) > 64
+    _, out = _run_step(w, num_splits=100)
+    assert_close(out.to(torch.float64).cpu().numpy(), expected(w), "86 splits")
+
+
+@pytest.mark.parametrize("block_size", [256, 16])
+def test_long_prefill_table_beyond_registers(block_size):
+    # one 12 k-token sequence whose first 8 k tokens are cached: at 16-token
+    # blocks its table has 768 entries, past the 128 a workgroup keeps in
+    # registers, so the copies read the rest through scalar loads; the last
+    # 512 query rows, sampled, against the oracle
+    ctx, new = 12288, 4096
+    w = build(Spec(f"pre-long-B{block_size}", "prefill", "bf16", 8, 2, [ctx], [new], 9202,
+                   block_size=block_size))
+    d, out = _run_step(w)
+    rows = list(range(new - 512, new, 7)) + [0, 1, 63, 64, 1000]
+    kcb, vcb = stored_bits(w)
+    want = ref.prefill(q64(w), ref.widen(kcb, "bf16"), ref.widen(vcb, "bf16"), w.cu_seqlens_q,
+                       w.context_lens, w.block_tables, w.scale, rows=rows)
+    got = out.to(torch.float64).cpu().numpy()
+    assert_close(got[rows], want[rows], f"long prefill at block size {block_size}")
+
+
 def test_split_partials_in_workspace():
     """The split-K partials (acc, m, l) the decode kernel leaves in the
     workspace match the oracle's partials for the same split size."""
