@@ -275,11 +275,13 @@ def traffic_for(kernel: str, workload: str):
     return rec["bytes"]
 
 
-def time_contiguous_prefill(d: Device, steps: int, torch):
+def time_contiguous_prefill(d: Device, steps: int, torch, settle_s: float = 0.5):
     """pkv_prefill_varlen (keys from contiguous rows, no block table) on the
     same keys as the paged prefill: every context row gathered once from the
     cache (after the store) into [total_k, Hkv, D].  Mean event-timed ms,
-    MALL evicted before each launch."""
+    MALL evicted before each launch, after ``settle_s`` seconds of
+    back-to-back launches (the gather leaves the GPU idle long enough for its
+    clocks to drop)."""
     import numpy as np
 
     import paged_kv_cache_325_amd as pkv
@@ -304,6 +306,11 @@ def time_contiguous_prefill(d: Device, steps: int, torch):
 
     flush = make_flush(torch)
     stream = torch.cuda.current_stream()
+    t_end = time.perf_counter() + settle_s
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            run()
+        torch.cuda.synchronize()
     for _ in range(3):
         flush()
         run()
