@@ -28,7 +28,10 @@ algorithmic bytes per launch over its mean event-timed duration, against the
 8 TB/s HBM peak.  ``cpu_baseline`` times the CPU oracle on the same workload
 (bounded to ~10 s, one thread).  ``extra`` reports the other workloads with
 the same method (prefill against the 2.5 PFLOP/s dense bf16 MFMA peak), and
-the same decode and prefill with cache blocks of 16, 32, 64 and 1024 tokens
+a 28-layer decode step (one fused step per layer, each layer with its own
+cache) launched eagerly and replayed from one captured graph
+(``decode-step-28-layers``), the same decode and prefill with cache blocks
+of 16, 32, 64 and 1024 tokens
 (``block-size-study``: attention time and fragmentation), and
 the host time of the block manager (C++ through the binding) for one decode
 step of 256 sequences and one prefill admission of 8 prompts; the oracle's
@@ -246,6 +249,59 @@ def time_fused_step(d: Device, steps: int, warmup: int, torch):
     graph_ms, _ = timed(graph.replay)
     del flush
     return eager_ms, wall, graph_ms
+
+
+def time_layer_stack(torch, index: int, layers: int = 28, reps: int = 20) -> dict:
+    """A model's decode step is one pkv_paged_decode_step per layer: the
+    step of ``layers`` layers (each with its own K/V cache, the same batch)
+    launched eagerly and replayed from one captured HIP graph, mean
+    event-timed microseconds per layer.  At small batch the eager step is
+    launch-bound and the graph removes the per-launch overhead (the pages
+    capture the decode step in graphs for this reason)."""
+    import paged_kv_cache_325_amd as pkv
+    from workloads import config
+
+    w = config(index)
+    d = Device(w, torch)
+    caches = [(d.k_cache.clone(), d.v_cache.clone()) for _ in range(layers)]
+
+    def step_all():
+        for kc, vc in caches:
+            pkv.pkv_paged_decode_step(d.q, d.k, d.v, d.slot_mapping, kc, vc, d.block_tables,
+                                      d.context_lens, w.max_context_len, w.scale, out=d.out,
+                                      workspace=d.workspace)
+
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return mean([e0.elapsed_time(e1) for e0, e1 in evs]) * 1e3 / layers
+
+    eager_us = timed(step_all)
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step_all()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step_all()
+    torch.cuda.synchronize()
+    graph_us = timed(graph.replay)
+    del graph, caches, d
+    torch.cuda.empty_cache()
+    return {"workload": w.spec.name, "layers": layers, "eager_us_per_layer": round(eager_us, 2),
+            "graph_us_per_layer": round(graph_us, 2)}
 
 
 # HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE runs (KiB per
@@ -637,6 +693,9 @@ def main() -> int:
                 "mean_launch_ms": round(head["attn_ms"], 5)}
 
     if not args.no_extra:
+        log("timing a 28-layer decode step, eager and from a captured graph")
+        extra["decode-step-28-layers"] = [time_layer_stack(torch, i) for i in (1, 2)]
+        log(f"28-layer decode step: {extra['decode-step-28-layers']}")
         log("timing other cache block sizes")
         extra["block-size-study"] = time_block_sizes(torch)
         log("timing the host block manager")
