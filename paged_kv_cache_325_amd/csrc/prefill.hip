@@ -150,8 +150,18 @@ __device__ __forceinline__ void tile_to_lds(__amdgpu_buffer_rsrc_t rsrc, const u
 // gfx9-family parts).  Loads past `bytes` return zero, so the rows of a
 // tile that lie past the context arrive in LDS as zeros: masked
 // probabilities are 0 and 0 * 0 stays 0 in the PV product.
+//
+// Every argument is the same in all lanes of the wave, but when it was
+// computed under a branch on the wave index (only group A copies) the
+// compiler cannot prove that and would wrap each copy in a loop over the
+// distinct resources of the lanes; readfirstlane states the uniformity.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, 0x00020000);
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), 0,
+      __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
@@ -281,9 +291,13 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4
           qb = block_of((uint32_t)k0);
           row = k0 - qb * bs;
         } else {
-          qb = cp_blk;
-          row = cp_row;
-          cp_row += kKT;
+          // uniform (see tile_rsrc): a lane-varying index would turn the
+          // table lookup into a vector load whose wait also waits for
+          // every copy still in flight
+          qb = __builtin_amdgcn_readfirstlane(cp_blk);
+          row = __builtin_amdgcn_readfirstlane(cp_row);
+          cp_row = row + kKT;
+          cp_blk = qb;
           if (cp_row == bs) cp_row = 0, ++cp_blk;
         }
         const int64_t blk = block_at((int)qb);
