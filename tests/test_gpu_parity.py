@@ -80,12 +80,14 @@ def test_decode_more_than_64_splits():
     assert_close(out.to(torch.float64).cpu().numpy(), expected(w), "86 splits")
 
 
-@pytest.mark.parametrize("block_size", [256, 16])
+@pytest.mark.parametrize("block_size", [256, 16, 64, 1024])
 def test_long_prefill_table_beyond_registers(block_size):
     # one 12 k-token sequence whose first 8 k tokens are cached: at 16-token
     # blocks its table has 768 entries, past the 128 a workgroup keeps in
-    # registers, so the copies read the rest through scalar loads; the last
-    # 512 query rows, sampled, against the oracle
+    # registers, so the copies read the rest through scalar loads (at 64:
+    # 192 entries, the block walker through all three sources; at 1024 the
+    # walker crosses a block every 16 tiles); the last 512 query rows,
+    # sampled, against the oracle
     ctx, new = 12288, 4096
     w = build(Spec(f"pre-long-B{block_size}", "prefill", "bf16", 8, 2, [ctx], [new], 9202,
                    block_size=block_size))
