@@ -251,3 +251,15 @@ def test_merge_errors():
     assert _merge(hq=24) == UNSUPPORTED
     assert _merge(splits=-1) == INVALID
     assert _merge(dtype=9) == INVALID
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without libpkv.so every entry point raises: there is no fallback path."""
+    monkeypatch.setattr(pkv, "_LIB", None)
+    monkeypatch.setattr(pkv, "lib_path", lambda: str(tmp_path / "libpkv.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        pkv.load_library()
+    with pytest.raises(RuntimeError, match="missing"):
+        pkv.pkv_kv_block_bytes(BF16, 8, 128, 256)
+    with pytest.raises(RuntimeError, match="missing"):
+        pkv.pkv_paged_decode_workspace_bytes(64, 16, 8, 128, 4096, 256, 0)
