@@ -30,7 +30,8 @@ algorithmic bytes per launch over its mean event-timed duration, against the
 the same method (prefill against the 2.5 PFLOP/s dense bf16 MFMA peak), and
 a 28-layer decode step (one fused step per layer, each layer with its own
 cache) launched eagerly and replayed from one captured graph
-(``decode-step-28-layers``), the same decode and prefill with cache blocks
+(``decode-step-28-layers``; the 4-sequence fp32 workload, batches of 1, 4
+and 16 of the 64-sequence workload's sequences, and all 64), the same decode and prefill with cache blocks
 of 16, 32, 64 and 1024 tokens
 (``block-size-study``: attention time and fragmentation), and
 the host time of the block manager (C++ through the binding) for one decode
@@ -251,7 +252,18 @@ def time_fused_step(d: Device, steps: int, warmup: int, torch):
     return eager_ms, wall, graph_ms
 
 
-def time_layer_stack(torch, index: int, layers: int = 28, reps: int = 20) -> dict:
+def decode_batch_bucket(nb: int):
+    """The first ``nb`` sequences of the 64-sequence decode workload (same
+    lengths, seed and head counts): the batch of one graph bucket."""
+    from workloads import Spec, build, config_specs
+
+    spec, _ = config_specs(2)
+    ctx = spec.context_lens[:nb]
+    return build(Spec(f"decode-bf16-b{nb}-ctx512-4096-h16-8", "decode", "bf16", spec.num_q_heads,
+                      spec.num_kv_heads, ctx, [1] * nb, spec.seed))
+
+
+def time_layer_stack(torch, w, layers: int = 28, reps: int = 20) -> dict:
     """A model's decode step is one pkv_paged_decode_step per layer: the
     step of ``layers`` layers (each with its own K/V cache, the same batch)
     launched eagerly and replayed from one captured HIP graph, mean
@@ -259,9 +271,7 @@ def time_layer_stack(torch, index: int, layers: int = 28, reps: int = 20) -> dic
     launch-bound and the graph removes the per-launch overhead (the pages
     capture the decode step in graphs for this reason)."""
     import paged_kv_cache_325_amd as pkv
-    from workloads import config
 
-    w = config(index)
     d = Device(w, torch)
     caches = [(d.k_cache.clone(), d.v_cache.clone()) for _ in range(layers)]
 
@@ -694,7 +704,9 @@ def main() -> int:
 
     if not args.no_extra:
         log("timing a 28-layer decode step, eager and from a captured graph")
-        extra["decode-step-28-layers"] = [time_layer_stack(torch, i) for i in (1, 2)]
+        from workloads import config
+        stacks = [config(1)] + [decode_batch_bucket(nb) for nb in (1, 4, 16)] + [config(2)]
+        extra["decode-step-28-layers"] = [time_layer_stack(torch, w) for w in stacks]
         log(f"28-layer decode step: {extra['decode-step-28-layers']}")
         log("timing other cache block sizes")
         extra["block-size-study"] = time_block_sizes(torch)

@@ -102,3 +102,101 @@ def test_step_replayed_from_graph():
         assert torch.equal(_bits(got), _bits(want)), f"replay {rep}: outputs differ"
         assert torch.equal(_bits(got_k), _bits(e.k_cache)), f"replay {rep}: k_cache differs"
         assert torch.equal(_bits(got_v), _bits(e.v_cache)), f"replay {rep}: v_cache differs"
+
+
+def test_graph_bucket_replays_with_padding():
+    """One decode step captured for a batch bucket of 8 sequences and a fixed
+    split plan (max_context_len 2048), then replayed for real batches of 8,
+    5, 1 and 3 sequences of other lengths: the metadata buffers are rewritten
+    in place and the unused rows padded with slot -1 and context 0.  Every
+    replay equals the eager step on the same buffers bitwise, padded rows are
+    zero and leave the caches untouched, and the real rows match the oracle."""
+    from tests.gpu_helpers import MAX_ABS, MEAN_ABS, errors
+    from tests.oracle_helpers import expected, to_numpy_out
+    from workloads import Spec
+
+    bucket, cap, B, pool = 8, 2048, 256, 64
+    cols = cap // B
+    hq, hkv, D = 8, 2, 128
+    cases = []
+    rng = np.random.default_rng(3251)
+    for r in (8, 5, 1, 3):
+        ctx = [int(x) for x in rng.integers(1, cap, size=r, endpoint=True)]
+        w = build(Spec(f"bucket-r{r}", "decode", "bf16", hq, hkv, ctx, [1] * r,
+                       int(rng.integers(1 << 30)), pool_blocks=pool))
+        assert w.block_tables.shape[1] <= cols and w.num_blocks == pool
+        cases.append(w)
+
+    def fill(dst, w):
+        """Copy workload w into the bucket-sized buffers, padding rows r.."""
+        r = w.batch
+        dst["qkv"].zero_()
+        dst["qkv"][:r].copy_(w.qkv.to("cuda"))
+        dst["slot"].fill_(-1)
+        dst["slot"][:r].copy_(torch.from_numpy(w.slot_mapping.astype(np.int32)))
+        dst["ctx"].zero_()
+        dst["ctx"][:r].copy_(torch.from_numpy(w.context_lens.astype(np.int32)))
+        dst["bt"].fill_(-1)
+        bt = torch.from_numpy(w.block_tables.astype(np.int32))
+        dst["bt"][:r, : bt.shape[1]].copy_(bt)
+        dst["kc"].copy_(w.k_cache.to("cuda"))
+        dst["vc"].copy_(w.v_cache.to("cuda"))
+
+    def buffers():
+        w0 = cases[0]
+        return {"qkv": torch.empty((bucket,) + tuple(w0.qkv.shape[1:]), dtype=w0.qkv.dtype, device="cuda"),
+                "slot": torch.empty(bucket, dtype=torch.int32, device="cuda"),
+                "ctx": torch.empty(bucket, dtype=torch.int32, device="cuda"),
+                "bt": torch.empty((bucket, cols), dtype=torch.int32, device="cuda"),
+                "kc": torch.empty_like(w0.k_cache, device="cuda"),
+                "vc": torch.empty_like(w0.v_cache, device="cuda"),
+                "out": torch.empty((bucket, hq, D), dtype=w0.qkv.dtype, device="cuda")}
+
+    need = pkv.pkv_paged_decode_workspace_bytes(bucket, hq, hkv, D, cap, B, 0)
+
+    def step(buf, ws):
+        q, k, v = buf["qkv"][:, :hq], buf["qkv"][:, hq:hq + hkv], buf["qkv"][:, hq + hkv:]
+        return pkv.pkv_paged_decode_step(q, k, v, buf["slot"], buf["kc"], buf["vc"], buf["bt"],
+                                         buf["ctx"], cap, cases[0].scale, out=buf["out"],
+                                         workspace=ws)
+
+    g_buf = buffers()
+    g_ws = torch.empty(max(need // 4, 1), dtype=torch.float32, device="cuda")
+    fill(g_buf, cases[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        announce("bucket graph: warm-up step")
+        step(g_buf, g_ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    announce("bucket graph: capture")
+    with torch.cuda.graph(graph):
+        step(g_buf, g_ws)
+    torch.cuda.synchronize()
+
+    e_buf = buffers()
+    e_ws = torch.empty(max(need // 4, 1), dtype=torch.float32, device="cuda")
+    for w in cases:
+        r = w.batch
+        fill(g_buf, w)
+        kc0, vc0 = g_buf["kc"].clone(), g_buf["vc"].clone()
+        torch.cuda.synchronize()
+        announce(f"bucket graph: replay with {r} real rows")
+        graph.replay()
+        torch.cuda.synchronize()
+        fill(e_buf, w)
+        announce(f"bucket graph: eager step with {r} real rows")
+        step(e_buf, e_ws)
+        torch.cuda.synchronize()
+        for key in ("out", "kc", "vc"):
+            assert torch.equal(_bits(g_buf[key]), _bits(e_buf[key])), f"r={r}: {key} differs"
+        assert not _bits(g_buf["out"][r:]).any(), f"r={r}: padded rows not zero"
+        # only the real rows' slots were written
+        changed = (_bits(g_buf["kc"]) != _bits(kc0)).any(dim=-1).nonzero()
+        written = {int(p) * B + int(o) for p, _, o in changed.tolist()}
+        assert written <= {int(s) for s in w.slot_mapping if s >= 0}, f"r={r}: stray cache writes"
+        got = to_numpy_out(g_buf["out"][:r])
+        mx, mean = errors(got, expected(w))
+        assert mx <= MAX_ABS and mean <= MEAN_ABS, f"r={r}: max {mx:.3e} mean {mean:.3e}"
