@@ -638,8 +638,10 @@ def main() -> int:
                     help="also run plain copies of a known size (for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the hot path is "
-              "measured on one GPU's share, see the design notes for sharding", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the hot path is "
+              "measured on one GPU's share.  Under tensor parallelism each GPU holds "
+              "num_kv_heads / tp kv heads and runs the same kernels on them, with no "
+              "exchange inside this path", file=sys.stderr)
         return 2
     if args.steps < 1 or args.warmup < 0:
         print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
