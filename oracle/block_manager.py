@@ -34,8 +34,7 @@ Sources, cited by page title and section (nano-vllm architecture page,
   源碼學習", hk.pswp.cn), section 1 "BlockManager": blocks are found by hash
   through a hash -> block id table.
 
-Readings where the pages are silent or only sketch a step (each also listed in
-the design notes):
+Readings where the pages are silent or only sketch a step:
   H1 the block hash is 64-bit FNV-1a (the published definition of Fowler,
      Noll and Vo: offset basis 0xcbf29ce484222325, prime 0x100000001b3, xor
      each byte then multiply) over the previous block's hash as 8

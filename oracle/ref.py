@@ -26,7 +26,7 @@ The attention formula itself is softmax(scale * q . k_j) weighted sum of v_j
 over the keys a query may see; the pages name the operation (decode and varlen
 causal prefill) but not the formula, so the plain textbook definition is used.
 
-Readings where the pages are silent (each also listed in the design notes):
+Readings where the pages are silent:
   * query head h uses kv head h // (Hq / Hkv) (contiguous GQA groups);
   * the store runs before attention and ``context_lens`` counts the stored
     token; a decode query sits at position ctx - 1;

@@ -2,7 +2,7 @@
 // built with AddressSanitizer and UndefinedBehaviorSanitizer by
 // tests/test_block_manager_sanitized.py.  A seeded stream of calls --
 // valid ones and deliberately invalid ones -- runs against the C ABI, and
-// after every call the driver checks, through the query entry points only:
+// after every call the program checks, through the query entry points only:
 //   * every block's count equals the number of tables holding it;
 //   * the free list holds exactly the blocks with count 0, each once;
 //   * a failing call changed nothing (state snapshot before and after);
