@@ -215,6 +215,23 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     if constexpr (kSmall) return chunk_base(c0 + i * S::kRowsPerLoad);
     else return cbase + i * 1024;
   };
+  // The K (or V) rows of the chunk at c0 into dst.  A chunk in one block is
+  // read through a buffer resource that covers only its rows inside the
+  // split, so the rows past the context in a sequence's last chunk arrive
+  // as zeros without being read (they are masked either way).  Blocks
+  // shorter than a chunk: one lookup and one plain load per 1 KiB.  With 8
+  // heads per workgroup the resource's registers would push the kernel
+  // past 256 VGPRs (one wave per SIMD instead of two), so that variant
+  // reads the whole chunk with plain loads.
+  constexpr bool kBounded = !kSmall && kHeads <= 4;
+  auto load_chunk = [&](u32x4 (&dst)[S::kLoads], const uint8_t* cache, int64_t cbase, int c0) {
+    if constexpr (kBounded) {
+      const __amdgpu_buffer_rsrc_t r =
+          bounded_rsrc(cache + cbase, min(kTok, end - c0) * S::kRowBytes);
+#pragma unroll
+      for (int i = 0; i < S::kLoads; ++i) dst[i] = stream_load(r, i * 1024 + lane * 16);
+    }
+  };
   // position whose K/V come from the fused store's input (-1: none here)
   int p_new = -1;
   if (slot_new >= 0 && n - 1 >= start && n - 1 < end) {
@@ -233,12 +250,17 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   u32x4 kr[S::kLoads], vr[S::kLoads];
   {
     const int64_t base = kSmall ? 0 : chunk_base(start);
+    if constexpr (!kBounded) {
 #pragma unroll
-    for (int i = 0; i < S::kLoads; ++i)
-      kr[i] = stream_load(a.k_cache + load_base(base, start, i) + lane * 16);
+      for (int i = 0; i < S::kLoads; ++i)
+        kr[i] = stream_load(a.k_cache + load_base(base, start, i) + lane * 16);
 #pragma unroll
-    for (int i = 0; i < S::kLoads; ++i)
-      vr[i] = stream_load(a.v_cache + load_base(base, start, i) + lane * 16);
+      for (int i = 0; i < S::kLoads; ++i)
+        vr[i] = stream_load(a.v_cache + load_base(base, start, i) + lane * 16);
+    } else {
+      load_chunk(kr, a.k_cache, base, start);
+      load_chunk(vr, a.v_cache, base, start);
+    }
   }
 
   auto chunk = [&](int c0, auto prefetch_tag, int64_t next_base) {
@@ -256,9 +278,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     if (sub && lane < kCPR) k_lds[(p_new - c0) * (kCPR + 1) + lane] = knew;
     __syncthreads();
     if constexpr (kPrefetch) {
+      if constexpr (!kBounded) {
 #pragma unroll
-      for (int i = 0; i < S::kLoads; ++i)
-        kr[i] = stream_load(a.k_cache + load_base(next_base, c_next, i) + lane * 16);
+        for (int i = 0; i < S::kLoads; ++i)
+          kr[i] = stream_load(a.k_cache + load_base(next_base, c_next, i) + lane * 16);
+      } else {
+        load_chunk(kr, a.k_cache, next_base, c_next);
+      }
     }
 
     const int nvalid = min(kTok, end - c0);
@@ -334,9 +360,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       }
     }
     if constexpr (kPrefetch) {
+      if constexpr (!kBounded) {
 #pragma unroll
-      for (int i = 0; i < S::kLoads; ++i)
-        vr[i] = stream_load(a.v_cache + load_base(next_base, c_next, i) + lane * 16);
+        for (int i = 0; i < S::kLoads; ++i)
+          vr[i] = stream_load(a.v_cache + load_base(next_base, c_next, i) + lane * 16);
+      } else {
+        load_chunk(vr, a.v_cache, next_base, c_next);
+      }
     }
   };
 

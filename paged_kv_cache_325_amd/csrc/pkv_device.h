@@ -54,6 +54,26 @@ __device__ __forceinline__ u32x4 stream_load(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// Raw buffer resource over `bytes` bytes at `base` (word 3: 32-bit data
+// format, the value used for untyped buffer access on gfx9-family parts).
+// A load at or past `bytes` returns zero and reads no memory.  Both
+// arguments must be the same in every lane; readfirstlane states that for
+// the compiler (otherwise a load through the resource may be wrapped in a
+// loop over the lanes' distinct values).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bounded_rsrc(const void* base, int bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), 0,
+                                           __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// 16-byte nontemporal load at byte offset `off` through a buffer resource
+// (cache policy: nt, as stream_load).
+__device__ __forceinline__ u32x4 stream_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Reductions over the 64 lanes of a wavefront; every lane gets the result.
