@@ -390,3 +390,36 @@ def test_config(index):
         want = ref.prefill(q, kc, vc, w.cu_seqlens_q, w.context_lens, w.block_tables, w.scale,
                            rows=rows)
         assert_close(out[rows], want[rows], f"config {index} sampled rows")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+@pytest.mark.parametrize("table_cols", [1, 0], ids=["table-1col", "table-0col"])
+def test_decode_all_contexts_empty(dtype, table_cols):
+    """A batch in which no sequence has a key (every context length 0,
+    max_context_len 0): every output row is written as 0 (no mass to
+    normalise), by the plain decode and by the fused step with every slot
+    -1, and the cache is left untouched."""
+    batch, hq, hkv, d, B = 3, 8, 2, 128, 256
+    g = torch.Generator().manual_seed(4711)
+    q = torch.randn(batch, hq, d, generator=g).to(dtype).cuda()
+    k_new = torch.randn(batch, hkv, d, generator=g).to(dtype).cuda()
+    v_new = torch.randn(batch, hkv, d, generator=g).to(dtype).cuda()
+    k_cache = torch.randn(1, hkv, B, d, generator=g).to(dtype).cuda()
+    v_cache = torch.randn(1, hkv, B, d, generator=g).to(dtype).cuda()
+    k0, v0 = k_cache.clone(), v_cache.clone()
+    tables = torch.full((batch, table_cols), -1, dtype=torch.int32, device="cuda")
+    ctx = torch.zeros(batch, dtype=torch.int32, device="cuda")
+    slots = torch.full((batch,), -1, dtype=torch.int32, device="cuda")
+    zeros = torch.zeros(batch, hq, d, dtype=dtype, device="cuda")
+    announce(f"all-empty decode, {dtype}, {table_cols} table columns")
+    out = torch.full((batch, hq, d), float("nan"), dtype=dtype, device="cuda")
+    pkv.pkv_paged_decode(q, k_cache, v_cache, tables, ctx, 0, 1 / math.sqrt(d), out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, zeros)
+    announce(f"all-empty fused decode step, {dtype}, {table_cols} table columns")
+    out2 = torch.full((batch, hq, d), float("nan"), dtype=dtype, device="cuda")
+    pkv.pkv_paged_decode_step(q, k_new, v_new, slots, k_cache, v_cache, tables, ctx, 0,
+                              1 / math.sqrt(d), out=out2)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, zeros)
+    assert torch.equal(k_cache, k0) and torch.equal(v_cache, v0)
