@@ -385,7 +385,8 @@ def config(index: int) -> Workload:
 def small_specs():
     """Parity cases the oracle finishes in seconds: several 64-token chunks,
     several blocks, ragged tails, GQA 1/2/4/8, fp32 and bf16, contexts of 1,
-    an empty context, shared prefixes, skipped stores and extra padding."""
+    an empty context, prefill sequences without query rows, shared prefixes,
+    skipped stores and extra padding."""
     out = []
     out.append(Spec("dec-bf16-g2-ragged", "decode", "bf16", 4, 2,
                     [1, 2, 63, 64, 65, 255, 256, 257, 511, 700, 1025, 2049], [1] * 12, 9001,
@@ -405,4 +406,8 @@ def small_specs():
                     [63, 64, 65, 129, 88], 9102))
     out.append(Spec("pre-bf16-g8", "prefill", "bf16", 8, 1, [200, 777], [200, 500], 9103))
     out.append(Spec("pre-bf16-peaked", "prefill", "bf16", 8, 2, [900, 300], [400, 300], 9104, q_scale=6.0))
+    # sequences with cached context but no query rows this step, first and
+    # in the middle, beside a single-row and a short fresh prompt
+    out.append(Spec("pre-bf16-zero-rows", "prefill", "bf16", 8, 2, [300, 5, 700, 256],
+                    [0, 5, 0, 1], 9105))
     return out
