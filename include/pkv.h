@@ -50,7 +50,7 @@
  *                        < 0 (or <= 0 where a size must be positive),
  *                        num_q_heads % num_kv_heads != 0, misalignment,
  *                        max_context_len > max_blocks_per_seq * block_size,
- *                        causal != 1;
+ *                        causal != 1, a scale that is not finite (NaN, +-inf);
  *   PKV_ERR_UNSUPPORTED  a block_size outside {16, 32, 64 k <= 4096},
  *                        head_dim != 128, a GQA group size
  *                        not in {1, 2, 4, 8} and not a multiple of 8, fp32
@@ -153,7 +153,9 @@ int32_t pkv_paged_decode_split_tokens(int32_t batch, int32_t num_q_heads,
  *                  token stored this step (the query sits at position
  *                  context_lens[b] - 1); 0 gives a zero output row
  *   max_context_len host; >= every context_lens[b]; sets the split plan
- *   scale          softmax scale (e.g. 1/sqrt(head_dim))
+ *   scale          softmax scale (e.g. 1/sqrt(head_dim)); any finite value,
+ *                  negative and zero included (zero gives the mean of the
+ *                  visible V rows)
  *   num_splits     0 = automatic; otherwise the requested number of splits
  *   out            device, [batch][num_q_heads][head_dim], dense, dtype
  *   workspace      device, >= pkv_paged_decode_workspace_bytes(...) bytes,
@@ -264,6 +266,7 @@ pkv_status pkv_paged_decode_merge(pkv_dtype dtype, const int32_t* context_lens,
  *                  step's store (cached prefix plus the n_q new tokens)
  *   max_context_len host; >= every n_k
  *   block_tables   as for decode
+ *   scale          softmax scale, any finite value (as for decode)
  *   causal         must be 1: query i of sequence b sits at position
  *                  n_k - n_q + i and sees keys 0 .. n_k - n_q + i
  *   out            device, [total_q][num_q_heads][head_dim], dense, bf16

@@ -1,5 +1,6 @@
 // C ABI of libpkv: argument checks, split planning and kernel launches.
 // Every check on host scalars and pointers happens before the first HIP call.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -226,7 +227,7 @@ pkv_status decode_parts(int parts, pkv_dtype dtype, const void* q, int64_t q_tok
     if ((st = check_stride("q_token_stride", q_token_stride, (int64_t)num_q_heads * head_dim,
                            eb)) != PKV_OK)
       return st;
-    if (!(scale == scale)) return fail(PKV_ERR_INVALID, "scale is NaN");
+    if (!isfinite(scale)) return fail(PKV_ERR_INVALID, "scale must be finite (got %g)", (double)scale);
   }
   if (fs) {
     if (!fs->k_new || !fs->v_new || !fs->slot_mapping || !k_cache || !v_cache)
@@ -371,7 +372,7 @@ pkv_status pkv_paged_prefill_varlen(pkv_dtype dtype, const void* q, int64_t q_to
   if ((st = check_stride("q_token_stride", q_token_stride, (int64_t)num_q_heads * head_dim, eb)) !=
       PKV_OK)
     return st;
-  if (!(scale == scale)) return fail(PKV_ERR_INVALID, "scale is NaN");
+  if (!isfinite(scale)) return fail(PKV_ERR_INVALID, "scale must be finite (got %g)", (double)scale);
   if (!workspace || ((uintptr_t)workspace & 3) != 0 ||
       workspace_bytes < pkv::prefill_workspace_bytes())
     return fail(PKV_ERR_WORKSPACE, "prefill workspace must be non-null, 4-byte aligned and >= %zu bytes",
@@ -429,7 +430,7 @@ pkv_status pkv_prefill_varlen(pkv_dtype dtype, const void* q, int64_t q_token_st
   // 64 key rows must stay inside one 32-bit buffer range
   if (k_token_stride * eb * 64 > INT32_MAX || v_token_stride * eb * 64 > INT32_MAX)
     return fail(PKV_ERR_UNSUPPORTED, "k/v token stride too large");
-  if (!(scale == scale)) return fail(PKV_ERR_INVALID, "scale is NaN");
+  if (!isfinite(scale)) return fail(PKV_ERR_INVALID, "scale must be finite (got %g)", (double)scale);
   if (!workspace || ((uintptr_t)workspace & 3) != 0 ||
       workspace_bytes < pkv::prefill_workspace_bytes())
     return fail(PKV_ERR_WORKSPACE, "prefill workspace must be non-null, 4-byte aligned and >= %zu bytes",

@@ -75,7 +75,13 @@ struct PrefillArgs {
   int32_t max_blocks;
   int32_t batch, num_q_heads, num_kv_heads, group;
   int32_t heads_per_wg, pos_tiles, head_chunks, max_wg_tiles;
-  float scale_log2;
+  float scale_log2;  // |scale| * log2(e), or log2(e) for a zero scale (> 0 either way)
+  // Applied to every 32-bit word (two bf16) of q: (word & q_keep) ^ q_flip.
+  // The kernel masks scores to -inf before scaling, which needs a positive
+  // scale; scale * q.k is computed exactly as |scale| * (-q).k for a
+  // negative scale (a sign flip of a bf16 is exact) and as 1 * (0 . k) for
+  // a zero one.
+  uint32_t q_keep, q_flip;
   uint16_t* out;
   // Keys from contiguous rows instead of the cache (no block table):
   // sequence b's keys are rows cu_k[b] .. cu_k[b+1]-1 of k_rows / v_rows.
@@ -233,7 +239,11 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4
     const int q_row = q_begin + min(qi, max(n_q - 1, 0));
     const uint16_t* qp = a.q + (int64_t)q_row * a.q_stride + (int64_t)h * kHeadDim + hf * 8;
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) qreg[kb] = *reinterpret_cast<const u32x4*>(qp + kb * 16);
+    for (int kb = 0; kb < 8; ++kb) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(qp + kb * 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qreg[kb][e] = (w[e] & a.q_keep) ^ a.q_flip;
+    }
   }
 
   f32x16 o_acc[4];
@@ -614,7 +624,9 @@ hipError_t launch_prefill(const PrefillLaunch& l, hipStream_t stream) {
   a.head_chunks = a.group / a.heads_per_wg;
   const int wg_rows = kQT * a.pos_tiles;
   a.max_wg_tiles = (l.max_seqlen_q + wg_rows - 1) / wg_rows;
-  a.scale_log2 = l.scale * kLog2e;
+  a.scale_log2 = (l.scale == 0.f ? 1.f : fabsf(l.scale)) * kLog2e;
+  a.q_keep = l.scale == 0.f ? 0u : 0xFFFFFFFFu;
+  a.q_flip = l.scale < 0.f ? 0x80008000u : 0u;
   a.out = (uint16_t*)l.out;
   const int64_t items = (int64_t)a.max_wg_tiles * l.batch * l.num_kv_heads * a.head_chunks;
   if (items <= 0) return hipSuccess;

@@ -127,7 +127,11 @@ def test_decode_errors():
     assert _decode(q=None) == INVALID
     assert _decode(out=FAKE + 8) == INVALID
     assert _decode(qs=100) == INVALID
-    assert _decode(scale=float("nan")) == INVALID
+    for bad in (float("nan"), float("inf"), float("-inf")):
+        assert _decode(scale=bad) == INVALID
+        assert _step(scale=bad) == INVALID
+    assert "finite" in pkv.pkv_last_error()
+    assert _decode(batch=0, scale=float("inf")) == OK  # no work: nothing is checked further
     assert _decode(splits=-2) == INVALID
     assert _decode(ws=None, wsb=0) == WORKSPACE
     need = pkv.pkv_paged_decode_workspace_bytes(4, 16, 8, 128, 4096, 256, 0)
@@ -185,6 +189,11 @@ def test_prefill_errors():
     assert _prefill(q=FAKE + 4) == INVALID
     assert _prefill(batch=-3) == INVALID
     assert "causal" in (_prefill(causal=2) and pkv.pkv_last_error())
+    # any finite scale is taken (negative and zero ones included); a
+    # non-finite one is refused
+    for bad in (float("nan"), float("inf"), float("-inf")):
+        assert _prefill(scale=bad) == INVALID
+    assert "finite" in pkv.pkv_last_error()
 
 
 def _prefill_contig(**kw):
@@ -210,6 +219,8 @@ def test_prefill_contiguous_errors():
     assert _prefill_contig(ks=8 * 128 - 8) == INVALID
     assert _prefill_contig(ws=None) == WORKSPACE
     assert "cu_seqlens_k" in (_prefill_contig(cuk=None) and pkv.pkv_last_error())
+    for bad in (float("nan"), float("inf"), float("-inf")):
+        assert _prefill_contig(scale=bad) == INVALID
 
 
 def test_prefill_workspace():

@@ -2,6 +2,8 @@
 paged prefill on the same keys (bitwise: same kernel, only the tile source
 differs) and against the fp64 oracle."""
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -50,6 +52,17 @@ def _both_paths(w):
 
 @pytest.mark.parametrize("spec", PREFILL_SMALL, ids=[s.name for s in PREFILL_SMALL])
 def test_contiguous_equals_paged_small(spec):
+    w = build(spec)
+    paged, contig = _both_paths(w)
+    assert torch.equal(paged.view(torch.int16), contig.view(torch.int16))
+    assert_close(contig.double().cpu().numpy(), expected(w), spec.name)
+
+
+@pytest.mark.parametrize("scale", [-0.25, 0.0])
+def test_contiguous_any_finite_scale(scale):
+    """Negative and zero scales through the contiguous tile source too."""
+    spec = dataclasses.replace(PREFILL_SMALL[0], scale=scale,
+                               name=f"{PREFILL_SMALL[0].name}-scale{scale:+.2f}")
     w = build(spec)
     paged, contig = _both_paths(w)
     assert torch.equal(paged.view(torch.int16), contig.view(torch.int16))
