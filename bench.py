@@ -132,7 +132,8 @@ class Device:
 
             def merge():
                 pkv.pkv_paged_decode_merge(self.context_lens, w.max_context_len, w.num_q_heads,
-                                           w.num_kv_heads, self.out, self.workspace)
+                                           w.num_kv_heads, w.block_size, self.out,
+                                           self.workspace)
 
             return [partials, merge]
 

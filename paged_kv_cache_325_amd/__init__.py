@@ -294,10 +294,16 @@ def pkv_paged_decode_partials(q, k_cache, v_cache, block_tables, context_lens, m
 
 
 def pkv_paged_decode_merge(context_lens: torch.Tensor, max_context_len: int, num_q_heads: int,
-                           num_kv_heads: int, out: torch.Tensor, workspace: Optional[torch.Tensor],
-                           num_splits: int = 0, stream=None) -> torch.Tensor:
+                           num_kv_heads: int, block_size: int, out: torch.Tensor,
+                           workspace: Optional[torch.Tensor], num_splits: int = 0,
+                           stream=None) -> torch.Tensor:
     """Second half of pkv_paged_decode: merge the partials in ``workspace``
-    into the rows of ``out`` [batch, Hq, D] whose sequences were split."""
+    into the rows of ``out`` [batch, Hq, D] whose sequences were split.
+
+    ``max_context_len``, ``block_size`` and ``num_splits`` must be those of
+    the partials call: together with the head counts they fix the split plan
+    (a split never spans more than 64 cache blocks, so the plan depends on
+    the block size)."""
     lib = load_library()
     _int32(context_lens, "context_lens")
     _gpu(out, "out")
@@ -309,9 +315,9 @@ def pkv_paged_decode_merge(context_lens: torch.Tensor, max_context_len: int, num
         _gpu(workspace, "workspace")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.pkv_paged_decode_merge(_dtype_code(out), _ptr(context_lens), int(max_context_len),
-                                      batch, int(num_q_heads), int(num_kv_heads), d, 256,
-                                      int(num_splits), _ptr(out), _ptr(workspace), ws_bytes,
-                                      _stream(stream)))
+                                      batch, int(num_q_heads), int(num_kv_heads), d,
+                                      int(block_size), int(num_splits), _ptr(out),
+                                      _ptr(workspace), ws_bytes, _stream(stream)))
     return out
 
 

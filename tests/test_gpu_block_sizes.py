@@ -15,7 +15,7 @@ import torch
 import paged_kv_cache_325_amd as pkv
 from tests.gpu_helpers import announce, assert_close, attend, check_inputs, store, to_device
 from tests.oracle_helpers import expected, stored_bits
-from workloads import bits_view, build, config, small_specs
+from workloads import Spec, bits_view, build, config, small_specs
 
 pytestmark = pytest.mark.gpu
 
@@ -158,3 +158,50 @@ def test_full_size_layout_invariance_bitwise(index, B2):
                                            d.context_lens, w.max_context_len, tab, w.scale)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+
+
+# (block size, requested splits, context lengths, q heads, kv heads).  With
+# 16- or 32-token blocks a split is capped at 64 blocks (1024 / 2048 keys), so
+# the plan differs from the one at 256-token blocks: a forced single split of
+# a 4096-key context becomes 4 (or 2) splits, and the automatic plan of a
+# 256-sequence batch with one 20000-key context (1024 units, splits of 2560
+# keys at 256-token blocks) is capped as well.  The merge must plan with the
+# caches' block size, or the rows of split sequences are never written.
+_LONG_AUTO = [20000, 9000, 3000] + [int(x) for x in
+                                    np.random.default_rng(9301).integers(1, 400, 253)]
+TWO_CALL_CASES = [
+    (16, 1, [4096, 1500, 700, 2049, 1], 8, 2),
+    (32, 1, [4096, 1500, 700, 2049, 1], 8, 2),
+    (16, 0, _LONG_AUTO, 8, 4),
+    (32, 0, _LONG_AUTO, 8, 4),
+]
+
+
+@pytest.mark.parametrize("B,splits,ctx,hq,hkv", TWO_CALL_CASES,
+                         ids=[f"B{c[0]}-splits{c[1]}-batch{len(c[2])}" for c in TWO_CALL_CASES])
+def test_two_call_decode_plans_with_block_size(B, splits, ctx, hq, hkv):
+    """pkv_paged_decode_partials then pkv_paged_decode_merge through the
+    binding at small blocks: bitwise equal to the one-call decode, every
+    output row written, and within tolerance of the oracle."""
+    w = build(Spec(f"two-call-B{B}-s{splits}", "decode", "bf16", hq, hkv, ctx, [1] * len(ctx),
+                   9300 + B + splits, block_size=B))
+    args = (w.batch, hq, hkv, 128, w.max_context_len)
+    here = pkv.pkv_paged_decode_split_tokens(*args, B, splits)
+    at256 = pkv.pkv_paged_decode_split_tokens(*args, 256, splits)
+    assert here < at256 and here < w.max_context_len, (here, at256)
+    d = to_device(w)
+    check_inputs(d)
+    announce(f"two-call decode at block size {B}, splits {splits}: store + one-call decode")
+    store(d)
+    whole = attend(d, num_splits=splits)
+    announce(f"two-call decode at block size {B}, splits {splits}: partials + merge")
+    out = torch.full_like(whole, float("nan"))
+    out, ws = pkv.pkv_paged_decode_partials(d.q, d.k_cache, d.v_cache, d.block_tables,
+                                            d.context_lens, w.max_context_len, w.scale,
+                                            out=out, num_splits=splits)
+    pkv.pkv_paged_decode_merge(d.context_lens, w.max_context_len, hq, hkv, B, out, ws,
+                               num_splits=splits)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out.float()).any(), "rows left unwritten by partials + merge"
+    assert torch.equal(whole.view(torch.int16), out.view(torch.int16))
+    assert_close(out.double().cpu().numpy(), expected(w), w.spec.name)
