@@ -17,19 +17,31 @@ def _key(cache, table, j, g, B):
     return cache[page][g][j % B]
 
 
+def scores(qv, cache_k, table, nkeys, g, B, scale):
+    """scale * (q . k_j) for keys j = 0 .. nkeys-1 of one sequence, each key
+    fetched cell by cell through its page and offset."""
+    out = []
+    for j in range(nkeys):
+        kr = _key(cache_k, table, j, g, B)
+        s = 0.0
+        for d in range(len(qv)):
+            s += qv[d] * kr[d]
+        out.append(s * scale)
+    return out
+
+
+def value_row(cache_v, table, j, g, B):
+    """V row of logical key j of one sequence (page and offset, as _key)."""
+    return _key(cache_v, table, j, g, B)
+
+
 def _attend_one(qv, cache_k, cache_v, table, nkeys, g, B, scale):
     D = len(qv)
     if nkeys <= 0:
         return [0.0] * D
-    scores = []
-    for j in range(nkeys):
-        kr = _key(cache_k, table, j, g, B)
-        s = 0.0
-        for d in range(D):
-            s += qv[d] * kr[d]
-        scores.append(s * scale)
-    top = max(scores)
-    ex = [math.exp(s - top) for s in scores]
+    scores_ = scores(qv, cache_k, table, nkeys, g, B, scale)
+    top = max(scores_)
+    ex = [math.exp(s - top) for s in scores_]
     tot = math.fsum(ex)
     out = [0.0] * D
     for j in range(nkeys):

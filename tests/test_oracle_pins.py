@@ -398,6 +398,51 @@ def test_split_partials_merge_to_decode(split):
         assert np.abs(ref.merge_partials(acc, m, l) - base[b]).max() < 1e-12
 
 
+def check_partials_against_brute_force(split=5):
+    """Largest deviation of the oracle's split partials from brute force on a
+    tiny paged case: m of a split must be the largest of its scores (taken
+    cell by cell through the block table), l the sum of exp(score - m) over
+    the split's keys and acc the sum of exp(score - m) * v over them.  (An
+    error in m alone cancels in the merge, so this pins m and l directly.)"""
+    rng = np.random.default_rng(31)
+    B, Hq, Hkv, D, nblk = 4, 4, 2, 8, 9
+    kc = rng.standard_normal((nblk, Hkv, B, D))
+    vc = rng.standard_normal((nblk, Hkv, B, D))
+    ctx = np.array([13, 4, 1, 9], dtype=np.int32)
+    tables = np.full((4, 4), -1, dtype=np.int32)
+    perm = rng.permutation(nblk)
+    tables[0, :4] = perm[:4]
+    tables[1, :1] = perm[4:5]
+    tables[2, :1] = perm[5:6]
+    tables[3, :3] = perm[6:9]
+    q = rng.standard_normal((4, Hq, D)) * 2.0
+    scale = 0.37
+    parts = ref.decode_partials(q, kc, vc, tables, ctx, scale, split)
+    worst = 0.0
+    for b in range(4):
+        acc, m, l = parts[b]
+        n = int(ctx[b])
+        assert acc.shape[0] == -(-n // split)
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            x = brute.scores(q[b][h].tolist(), kc.tolist(), tables[b].tolist(), n, g, B, scale)
+            for s in range(acc.shape[0]):
+                lo, hi = s * split, min(n, (s + 1) * split)
+                top = max(x[lo:hi])
+                e = [math.exp(v - top) for v in x[lo:hi]]
+                a = [math.fsum(e[j - lo] * brute.value_row(vc.tolist(), tables[b].tolist(), j,
+                                                            g, B)[d] for j in range(lo, hi))
+                     for d in range(D)]
+                worst = max(worst, abs(m[s, h] - top), abs(l[s, h] - math.fsum(e)) / math.fsum(e),
+                            float(np.abs(acc[s, h] - np.array(a)).max()))
+    return worst
+
+
+@pytest.mark.parametrize("split", [1, 3, 5, 64])
+def test_split_partials_against_brute_force(split):
+    assert check_partials_against_brute_force(split) < 1e-12
+
+
 # ---------------------------------------------------------------------------
 # planted mistakes: each plausible error in the oracle fails a pin above
 # ---------------------------------------------------------------------------
@@ -428,6 +473,23 @@ def test_planted_mistakes_are_caught(monkeypatch):
         m.setattr(ref, "prefill_contiguous",
                   lambda q, k, v, cq, ck, s, rows=None: orig_c(q, v, k, cq, ck, s, rows))
         assert check_sdpa_prefill_contiguous() > 1e-3
+    with monkeypatch.context() as m:  # split maxima offset (cancels in the merge)
+        orig_p = ref.decode_partials
+
+        def shifted(*a, **k):
+            return [(acc, mm + 1.0, l) for acc, mm, l in orig_p(*a, **k)]
+        m.setattr(ref, "decode_partials", shifted)
+        assert check_partials_against_brute_force() > 0.5
+    with monkeypatch.context() as m:  # split sums taken over the whole sequence
+        orig_p = ref.decode_partials
+
+        def whole_l(q, kc, vc, bt, ctx, scale, split):
+            full = orig_p(q, kc, vc, bt, ctx, scale, 1 << 30)
+            return [(acc, mm, np.broadcast_to(fl[0], l.shape).copy())
+                    for (acc, mm, l), (_, _, fl) in zip(orig_p(q, kc, vc, bt, ctx, scale, split),
+                                                        full)]
+        m.setattr(ref, "decode_partials", whole_l)
+        assert check_partials_against_brute_force() > 1e-3
     with monkeypatch.context() as m:  # off-by-one in the number of blocks read
         m.setattr(ref, "num_blocks", lambda n, B: n // B + 1 if n % B else n // B - 1 if n > B else 1)
         with pytest.raises(Exception):
