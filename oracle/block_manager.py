@@ -107,29 +107,11 @@ def compute_hash(token_ids, prefix: int = -1) -> int:
     return fnv1a64(block_hash_bytes(token_ids, prefix)) & ((1 << 63) - 1)
 
 
-class Block:
-    """One physical block (architecture page, "Block-Struktur und
-    Referenzzählung")."""
-
-    def __init__(self, block_id: int):
-        self.block_id = block_id
-        self.ref_count = 0
-        self.hash = -1
-        self.token_ids: list[int] = []
-
-    def update(self, h: int, token_ids) -> None:
-        self.hash = h
-        self.token_ids = list(token_ids)
-
-    def reset(self) -> None:
-        self.ref_count = 1
-        self.hash = -1
-        self.token_ids = []
-
-
 class Sequence:
     """The block-manager view of one request (architecture page, "Sequenz-
-    Status und Eigenschaften", "Block-Berechnung und Token-Appending")."""
+    Status und Eigenschaften", "Block-Berechnung und Token-Appending"): its
+    token ids, the physical blocks holding them in logical order, and how
+    many leading tokens were found in the cache when it was admitted."""
 
     def __init__(self, seq_id: int, token_ids, block_size: int):
         self.seq_id = seq_id
@@ -143,7 +125,8 @@ class Sequence:
 
     @property
     def num_blocks(self) -> int:
-        return (len(self) + self.block_size - 1) // self.block_size
+        """ceil(len / B)."""
+        return -(-len(self.token_ids) // self.block_size)
 
     @property
     def num_cached_blocks(self) -> int:
@@ -151,101 +134,157 @@ class Sequence:
 
     @property
     def last_block_num_tokens(self) -> int:
-        return len(self) - (self.num_blocks - 1) * self.block_size
+        """Tokens held by the last block: len - (num_blocks - 1) B."""
+        return len(self.token_ids) - (self.num_blocks - 1) * self.block_size
 
     def block(self, i: int) -> list[int]:
-        return self.token_ids[i * self.block_size:(i + 1) * self.block_size]
+        """Token ids of logical block i."""
+        lo = i * self.block_size
+        return self.token_ids[lo:lo + self.block_size]
 
     def append_token(self, token_id: int) -> None:
         self.token_ids.append(int(token_id))
 
 
 class BlockManager:
-    """Block pool with reference counts and hash-based prefix sharing
-    (architecture page, "Hash-basiertes Prefix Caching", "Dynamische
-    Block-Erweiterung")."""
+    """A pool of ``num_blocks`` physical blocks with reference counts and
+    hash-based prefix sharing (architecture page, "Block-Struktur und
+    Referenzzählung", "Hash-basiertes Prefix Caching", "Dynamische
+    Block-Erweiterung").
+
+    State, one entry per physical block:
+      count[b]     number of sequences whose table holds b (0: b is free);
+      recorded[b]  (hash, tokens) b was registered with when it held a full
+                   block, or None; kept when b is given back (H5) and
+                   dropped when b is handed out for new contents (H4);
+    and for the pool:
+      index        hash -> the block most recently registered under it
+                   (an entry can be stale, see H9);
+      free         the free blocks in hand-out order (front first).
+    """
 
     def __init__(self, num_blocks: int, block_size: int):
         assert num_blocks >= 1 and block_size >= 2  # at 1 a token opens and fills a block
         self.block_size = block_size
-        self.blocks = [Block(i) for i in range(num_blocks)]
-        self.hash_to_block_id: dict[int, int] = {}
-        self.free_block_ids: list[int] = list(range(num_blocks))  # front = index 0
-        self.used_block_ids: set[int] = set()
+        self.count = [0] * num_blocks
+        self.recorded: list = [None] * num_blocks
+        self.index: dict[int, int] = {}
+        self.free: list[int] = list(range(num_blocks))
 
-    # -- single blocks ------------------------------------------------------
-    def _allocate_block(self, block_id: int) -> Block:
-        block = self.blocks[block_id]
-        assert block.ref_count == 0
-        block.reset()
-        self.free_block_ids.remove(block_id)
-        self.used_block_ids.add(block_id)
-        return block
+    def state(self, b: int):
+        """(count, registered hash or -1, number of recorded tokens) of block b."""
+        rec = self.recorded[b]
+        return self.count[b], (-1 if rec is None else rec[0]), (0 if rec is None else len(rec[1]))
 
-    def _deallocate_block(self, block_id: int) -> None:
-        assert self.blocks[block_id].ref_count == 0
-        self.used_block_ids.remove(block_id)
-        self.free_block_ids.append(block_id)
+    # -- moves of single blocks ----------------------------------------------
+    def _fresh(self) -> int:
+        """Hand out the front free block for new contents (H4)."""
+        b = self.free.pop(0)
+        assert self.count[b] == 0
+        self.count[b] = 1
+        self.recorded[b] = None
+        return b
 
-    # -- sequences -------------------------------------------------------------
+    def _take(self, b: int) -> None:
+        """One more sequence holds cached block b; a given-back block leaves
+        the free list (H3)."""
+        if self.count[b] == 0:
+            self.free.remove(b)
+        self.count[b] += 1
+
+    def _register(self, b: int, h: int, tokens) -> None:
+        """Block b now holds a full block with chained hash h (H4, H7)."""
+        self.recorded[b] = (h, tuple(tokens))
+        self.index[h] = b
+
+    def _holds(self, b: int, h: int, tokens) -> bool:
+        """Block b is registered under h with exactly these tokens (H9)."""
+        return self.recorded[b] == (h, tuple(tokens))
+
+    # -- allocation -------------------------------------------------------------
+    def chained_hashes(self, seq: Sequence) -> list[int]:
+        """One entry per logical block: the hash of a full block, chained on
+        the hash of the block before it (H1); -1 for a partial last block."""
+        out, prev = [], -1
+        for i in range(seq.num_blocks):
+            tokens = seq.block(i)
+            if len(tokens) < self.block_size:
+                out.append(-1)
+            else:
+                prev = compute_hash(tokens, prev)
+                out.append(prev)
+        return out
+
+    def cache_hits(self, seq: Sequence, hashes) -> list[bool]:
+        """Which logical blocks are served from the cache: the longest run of
+        leading blocks whose hash finds a block holding that hash and those
+        tokens (H2: nothing after the first miss; H9)."""
+        hits = []
+        for i, h in enumerate(hashes):
+            b = self.index.get(h) if h != -1 else None
+            if b is None or not self._holds(b, h, seq.block(i)) or (hits and not hits[-1]):
+                hits.append(False)
+            else:
+                hits.append(True)
+        return hits
+
     def can_allocate(self, seq: Sequence) -> bool:
-        return len(self.free_block_ids) >= seq.num_blocks  # H6
+        return len(self.free) >= seq.num_blocks  # H6
 
     def allocate(self, seq: Sequence) -> None:
+        """Give a newly admitted sequence its blocks: cached ones for its
+        cache hits, fresh ones from the front of the free list for the rest;
+        every full block ends up registered under its chained hash."""
         assert not seq.block_table
-        h = -1
-        missed = False
-        for i in range(seq.num_blocks):
-            token_ids = seq.block(i)
-            h = compute_hash(token_ids, h) if len(token_ids) == self.block_size else -1
-            block_id = self.hash_to_block_id.get(h, -1)
-            if (block_id == -1 or self.blocks[block_id].hash != h  # H9
-                    or self.blocks[block_id].token_ids != token_ids):
-                missed = True  # H2: no hit after the first miss
-            if missed:
-                block = self._allocate_block(self.free_block_ids[0])  # H4
+        hashes = self.chained_hashes(seq)
+        hits = self.cache_hits(seq, hashes)
+        table = []
+        for i, (h, hit) in enumerate(zip(hashes, hits)):
+            if hit:
+                b = self.index[h]
+                self._take(b)
             else:
-                seq.num_cached_tokens += self.block_size
-                if block_id in self.used_block_ids:
-                    block = self.blocks[block_id]
-                    block.ref_count += 1
-                else:  # H3: given back but still registered
-                    block = self._allocate_block(block_id)
+                b = self._fresh()
             if h != -1:
-                block.update(h, token_ids)
-                self.hash_to_block_id[h] = block.block_id
-            seq.block_table.append(block.block_id)
+                self._register(b, h, seq.block(i))
+            table.append(b)
+        seq.block_table = table
+        seq.num_cached_tokens = self.block_size * sum(hits)
 
     def deallocate(self, seq: Sequence) -> None:
-        for block_id in reversed(seq.block_table):  # H5
-            block = self.blocks[block_id]
-            block.ref_count -= 1
-            if block.ref_count == 0:
-                self._deallocate_block(block_id)
+        """Give back a finished or preempted sequence's blocks, last logical
+        block first; a block nobody holds any more joins the back of the free
+        list with its registration intact (H5)."""
+        for b in seq.block_table[::-1]:
+            self.count[b] -= 1
+            if self.count[b] == 0:
+                self.free.append(b)
         seq.num_cached_tokens = 0
         seq.block_table = []
 
+    # -- decode growth ------------------------------------------------------------
     def can_append(self, seq: Sequence) -> bool:
-        need = 1 if len(seq) % self.block_size == 1 else 0  # H6
-        return len(self.free_block_ids) >= need
+        opens_block = len(seq) % self.block_size == 1
+        return len(self.free) >= (1 if opens_block else 0)  # H6
 
     def may_append(self, seq: Sequence) -> None:
-        table = seq.block_table
-        last = self.blocks[table[-1]]
-        r = len(seq) % self.block_size
-        if r == 1:  # the new token opens a block
-            assert last.hash != -1
-            block = self._allocate_block(self.free_block_ids[0])
-            table.append(block.block_id)
-        elif r == 0:  # the new token fills the last block (H7)
-            assert last.hash == -1
-            token_ids = seq.block(seq.num_blocks - 1)
-            prefix = self.blocks[table[-2]].hash if len(table) > 1 else -1
-            h = compute_hash(token_ids, prefix)
-            last.update(h, token_ids)
-            self.hash_to_block_id[h] = last.block_id
+        """After a decoded token was appended (H7): a token that opens a block
+        gets a fresh one; a token that fills the last block seals it (hash
+        chained on the previous block's, tokens recorded, entered in the
+        index); any other token needs nothing."""
+        fill = len(seq) % self.block_size
+        last = seq.block_table[-1]
+        if fill == 1:
+            assert self.recorded[last] is not None
+            seq.block_table.append(self._fresh())
+        elif fill == 0:
+            assert self.recorded[last] is None
+            tail = seq.block_table[-2] if len(seq.block_table) > 1 else None
+            prev = -1 if tail is None else self.recorded[tail][0]
+            tokens = seq.block(seq.num_blocks - 1)
+            self._register(last, compute_hash(tokens, prev), tokens)
         else:
-            assert last.hash == -1
+            assert self.recorded[last] is None
 
 
 # -- per-step metadata (architecture page, "Prefill- und Decode-Vorbereitung")

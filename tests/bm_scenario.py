@@ -57,11 +57,10 @@ class OracleAdapter:
         return len(self.seqs[sid])
 
     def free(self):
-        return list(self.bm.free_block_ids)
+        return list(self.bm.free)
 
     def block(self, b):
-        blk = self.bm.blocks[b]
-        return blk.ref_count, blk.hash, len(blk.token_ids)
+        return self.bm.state(b)
 
     def prefill_meta(self, sids, width):
         return self.m.prepare_prefill([self.seqs[s] for s in sids], width)

@@ -80,9 +80,9 @@ def _check_invariants(kind, batch, adapters):
             counts[b] = counts.get(b, 0) + 1
     free = a.free()
     assert len(free) == len(set(free))
-    for b, blk in enumerate(a.bm.blocks):
-        assert blk.ref_count == counts.get(b, 0), f"block {b} count"
-        assert (blk.ref_count == 0) == (b in free), f"block {b} free-list membership"
+    for b in range(len(a.bm.count)):
+        assert a.bm.count[b] == counts.get(b, 0), f"block {b} count"
+        assert (a.bm.count[b] == 0) == (b in free), f"block {b} free-list membership"
     # sequences of this step have had their table brought up to their length
     # (allocate or may_append); the other running ones hold a sampled token
     # that their next decode step's may_append will place
@@ -92,14 +92,15 @@ def _check_invariants(kind, batch, adapters):
         assert seq.num_cached_tokens % B == 0 and seq.num_cached_tokens <= len(seq)
         prefix = -1
         for i, b in enumerate(seq.block_table[:-1] if len(seq) % B else seq.block_table):
-            blk = a.bm.blocks[b]
-            assert blk.token_ids == seq.block(i), "a full block records its tokens"
             h = bm.fnv1a64(bm.block_hash_bytes(seq.block(i), prefix)) & (2 ** 63 - 1)
-            assert blk.hash == h, "a full block carries the chained hash of its sequence"
+            assert a.bm.recorded[b] is not None, "a full block is registered"
+            assert list(a.bm.recorded[b][1]) == seq.block(i), "a full block records its tokens"
+            assert a.bm.recorded[b][0] == h, \
+                "a full block carries the chained hash of its sequence"
             prefix = h
     if kind == "decode":
         for s in batch:  # the block holding the decoded token is private
-            assert a.bm.blocks[a.seqs[s].block_table[-1]].ref_count == 1
+            assert a.bm.count[a.seqs[s].block_table[-1]] == 1
 
 
 @pytest.mark.parametrize("seed", [1, 2, 3])
@@ -125,7 +126,7 @@ def _fails(fn):
 
 def test_planted_mistakes_are_caught(monkeypatch):
     cls = bm.BlockManager
-    orig = {name: getattr(cls, name) for name in ("allocate",)}
+    orig_allocate = cls.allocate
 
     # 1. hash not chained on the previous block
     with monkeypatch.context() as m:
@@ -134,62 +135,26 @@ def test_planted_mistakes_are_caught(monkeypatch):
         _fails(test_golden_scenario)
 
     # 2. hit tested on tokens only (reading H9 dropped)
-    def allocate_no_h9(self, seq):
-        h, missed = -1, False
-        for i in range(seq.num_blocks):
-            t = seq.block(i)
-            h = bm.compute_hash(t, h) if len(t) == self.block_size else -1
-            b = self.hash_to_block_id.get(h, -1)
-            missed = missed or b == -1 or self.blocks[b].token_ids != t
-            if missed:
-                blk = self._allocate_block(self.free_block_ids[0])
-            else:
-                seq.num_cached_tokens += self.block_size
-                if b in self.used_block_ids:
-                    blk = self.blocks[b]
-                    blk.ref_count += 1
-                else:
-                    blk = self._allocate_block(b)
-            if h != -1:
-                blk.update(h, t)
-                self.hash_to_block_id[h] = blk.block_id
-            seq.block_table.append(blk.block_id)
-
     with monkeypatch.context() as m:
-        m.setattr(cls, "allocate", allocate_no_h9)
+        m.setattr(cls, "_holds", lambda self, b, h, toks: self.recorded[b] is not None
+                  and self.recorded[b][1] == tuple(toks))
         _fails(test_golden_scenario)
 
     # 3. no miss-latch: hits allowed after a miss (reading H2 dropped)
-    def allocate_no_h2(self, seq):
-        h = -1
-        for i in range(seq.num_blocks):
-            t = seq.block(i)
-            h = bm.compute_hash(t, h) if len(t) == self.block_size else -1
-            b = self.hash_to_block_id.get(h, -1)
-            if b == -1 or self.blocks[b].hash != h or self.blocks[b].token_ids != t:
-                blk = self._allocate_block(self.free_block_ids[0])
-            else:
-                seq.num_cached_tokens += self.block_size
-                if b in self.used_block_ids:
-                    blk = self.blocks[b]
-                    blk.ref_count += 1
-                else:
-                    blk = self._allocate_block(b)
-            if h != -1:
-                blk.update(h, t)
-                self.hash_to_block_id[h] = blk.block_id
-            seq.block_table.append(blk.block_id)
+    def hits_anywhere(self, seq, hashes):
+        return [h != -1 and self.index.get(h) is not None
+                and self._holds(self.index[h], h, seq.block(i)) for i, h in enumerate(hashes)]
 
     with monkeypatch.context() as m:
-        m.setattr(cls, "allocate", allocate_no_h2)
+        m.setattr(cls, "cache_hits", hits_anywhere)
         _fails(lambda: test_collision_does_not_cache_a_non_prefix_block(m))
 
     # 4. deallocate first-to-last instead of last-to-first
     def deallocate_forward(self, seq):
         for b in seq.block_table:
-            self.blocks[b].ref_count -= 1
-            if self.blocks[b].ref_count == 0:
-                self._deallocate_block(b)
+            self.count[b] -= 1
+            if self.count[b] == 0:
+                self.free.append(b)
         seq.num_cached_tokens = 0
         seq.block_table = []
 
@@ -199,45 +164,27 @@ def test_planted_mistakes_are_caught(monkeypatch):
 
     # 5. a miss takes the back of the free list
     with monkeypatch.context() as m:
-        def alloc_back(self, seq, _orig=orig["allocate"]):
-            self.free_block_ids.reverse()
+        def alloc_back(self, seq):
+            self.free.reverse()
             try:
-                _orig(self, seq)
+                orig_allocate(self, seq)
             finally:
-                self.free_block_ids.reverse()
+                self.free.reverse()
         m.setattr(cls, "allocate", alloc_back)
         _fails(test_golden_scenario)
 
     # 6. a hit on a freed block is counted but left in the free list
-    def allocate_h3_wrong(self, seq):
-        h, missed = -1, False
-        for i in range(seq.num_blocks):
-            t = seq.block(i)
-            h = bm.compute_hash(t, h) if len(t) == self.block_size else -1
-            b = self.hash_to_block_id.get(h, -1)
-            missed = missed or b == -1 or self.blocks[b].hash != h or \
-                self.blocks[b].token_ids != t
-            if missed:
-                blk = self._allocate_block(self.free_block_ids[0])
-            else:
-                seq.num_cached_tokens += self.block_size
-                blk = self.blocks[b]
-                blk.ref_count += 1  # wrong for a freed block: it stays in the free list
-                self.used_block_ids.add(b)
-            if h != -1:
-                blk.update(h, t)
-                self.hash_to_block_id[h] = blk.block_id
-            seq.block_table.append(blk.block_id)
+    def take_in_place(self, b):
+        self.count[b] += 1
 
     with monkeypatch.context() as m:
-        m.setattr(cls, "allocate", allocate_h3_wrong)
+        m.setattr(cls, "_take", take_in_place)
         _fails(test_golden_scenario)
 
     # 7. may_append opens a block when the last one fills (off by one)
     def may_append_off(self, seq):
         if len(seq) % self.block_size == 0:
-            blk = self._allocate_block(self.free_block_ids[0])
-            seq.block_table.append(blk.block_id)
+            seq.block_table.append(self._fresh())
 
     with monkeypatch.context() as m:
         m.setattr(cls, "may_append", may_append_off)
@@ -273,7 +220,20 @@ def test_planted_mistakes_are_caught(monkeypatch):
     # 10. can_append asks for a block when the last one is full (len % B == 0)
     with monkeypatch.context() as m:
         m.setattr(cls, "can_append",
-                  lambda self, seq: len(self.free_block_ids) >= (len(seq) % self.block_size == 0))
+                  lambda self, seq: len(self.free) >= (len(seq) % self.block_size == 0))
+        _fails(test_golden_scenario)
+
+    # 11. a freed block forgets its registration (reading H5: it keeps it)
+    with monkeypatch.context() as m:
+        orig_dealloc = cls.deallocate
+
+        def dealloc_forget(self, seq):
+            held = list(seq.block_table)
+            orig_dealloc(self, seq)
+            for b in held:
+                if self.count[b] == 0:
+                    self.recorded[b] = None
+        m.setattr(cls, "deallocate", dealloc_forget)
         _fails(test_golden_scenario)
 
     # the unpatched oracle still passes
