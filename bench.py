@@ -1,7 +1,7 @@
 """Benchmark of the paged KV-cache hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle S] [--workload 2]
-                    [--no-extra] [--no-cpu] [--copy-calibration]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle S] [--workload 4]
+                    [--no-extra] [--no-cpu] [--cpu-budget S] [--copy-calibration]
 
 One step = the whole per-layer hot path over one batch of the workload: the
 store of this step's K/V tokens into the cache, then attention over the cache,
@@ -16,27 +16,33 @@ KV cache from HBM.  The eviction reads rather than writes: a write would leave
 up to 256 MB of dirty lines whose write-back would then be charged to the
 measured step.  Before the warm-up steps the step runs back to back for
 ``--settle`` seconds (default 1) so that the GPU has left its idle clocks.
-The step itself is timed with HIP events recorded on the
-stream the kernels run on, which excludes the eviction.  The timed region (K steps) is
-bracketed by device synchronisation.
+Every launch is timed with HIP events recorded on the stream the kernels run
+on, which excludes the eviction; figures are medians over the timed steps.
+The timed region (K steps) is bracketed by device synchronisation.
 
-The headline line is the 64-sequence bf16 decode layer (context lengths
-U[512, 4096], 16 q / 8 kv heads).  ``value`` is the step's algorithmic bytes
-(stored K/V rows read and written, the context's K and V, q and out) per
-second.  ``roofline`` covers the dominant kernel, the decode kernel: its
-algorithmic bytes per launch over its mean event-timed duration, against the
-8 TB/s HBM peak.  ``cpu_baseline`` times the CPU oracle on the same workload
-(bounded to ~10 s, one thread).  ``extra`` reports the other workloads with
-the same method (prefill against the 2.5 PFLOP/s dense bf16 MFMA peak), and
-a 28-layer decode step (one fused step per layer, each layer with its own
-cache) launched eagerly and replayed from one captured graph
+The headline line is the largest workload, the 256-sequence bf16 decode
+layer (context lengths U[1024, 8192], 32 q / 8 kv heads, 4.8 GB of K/V).
+``value`` is the step's algorithmic bytes (stored K/V rows read and written,
+the context's K and V, q and out) per second.  ``roofline`` covers the
+dominant kernel, the decode split kernel: its algorithmic bytes per launch
+over its mean event-timed duration (the figure rocprofv3's average is
+compared with), against the 8 TB/s HBM peak.  ``headline`` and ``extra``
+give every workload's times and the fraction of its roofline each part
+reaches (decode: the partials kernel, partials + merge, the fused step, and
+for the prefix-shared workload the same on unique bytes; prefill: against
+the 2.5 PFLOP/s dense bf16 MFMA peak).  ``cpu_baseline`` times the CPU oracle
+as it stands on the host's cores (the headline workload, and every other one
+under ``per_workload``), bounded to ``--cpu-budget`` seconds of work each,
+with the core count and the sample stated.  ``extra`` also holds a 28-layer
+decode step (one fused step per layer, each layer with its own cache)
+launched eagerly and replayed from one captured graph
 (``decode-step-28-layers``; the 4-sequence fp32 workload, batches of 1, 4
-and 16 of the 64-sequence workload's sequences, and all 64), the same decode and prefill with cache blocks
-of 16, 32, 64 and 1024 tokens
-(``block-size-study``: attention time and fragmentation), and
-the host time of the block manager (C++ through the binding) for one decode
-step of 256 sequences and one prefill admission of 8 prompts; the oracle's
-time for the same appears under ``cpu_baseline.block_manager``.
+and 16 of the 64-sequence workload's sequences, and all 64), the 64-sequence
+decode and the prefill with cache blocks of 16, 32, 64 and 1024 tokens
+(``block-size-study``: attention time and fragmentation), and the host time
+of the block manager (C++ through the binding) for one decode step of 256
+sequences and one prefill admission of 8 prompts; the oracle's time for the
+same appears under ``cpu_baseline.block_manager``.
 Prints exactly one JSON line on stdout.
 """
 
@@ -202,12 +208,18 @@ def mean(x):
     return sum(x) / len(x)
 
 
+def median(x):
+    y = sorted(x)
+    n = len(y)
+    return y[n // 2] if n % 2 else 0.5 * (y[n // 2 - 1] + y[n // 2])
+
+
 def time_fused_step(d: Device, steps: int, warmup: int, torch):
     """The decode step as one call (pkv_paged_decode_step: store fused into
     the decode): ``warmup`` untimed steps, then exactly ``steps`` timed ones
     between device synchronisations, MALL evicted before each step as in
-    time_steps.  Returns (mean event-timed ms, wall seconds of the timed
-    region, mean ms of the same step replayed from a captured graph)."""
+    time_steps.  Returns (median event-timed ms, wall seconds of the timed
+    region, median ms of the same step replayed from a captured graph)."""
     import paged_kv_cache_325_amd as pkv
 
     w = d.w
@@ -235,7 +247,7 @@ def time_fused_step(d: Device, steps: int, warmup: int, torch):
             e1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        return mean([e0.elapsed_time(e1) for e0, e1 in evs]), wall
+        return median([e0.elapsed_time(e1) for e0, e1 in evs]), wall
 
     eager_ms, wall = timed(step)
     side = torch.cuda.Stream()
@@ -295,7 +307,7 @@ def time_layer_stack(torch, w, layers: int = 28, reps: int = 20) -> dict:
             fn()
             e1.record(stream)
         torch.cuda.synchronize()
-        return mean([e0.elapsed_time(e1) for e0, e1 in evs]) * 1e3 / layers
+        return median([e0.elapsed_time(e1) for e0, e1 in evs]) * 1e3 / layers
 
     eager_us = timed(step_all)
     side = torch.cuda.Stream()
@@ -320,6 +332,9 @@ def time_layer_stack(torch, w, layers: int = 28, reps: int = 20) -> dict:
 # the sha256 of the kernel source they were taken on: once the source
 # changes, the figure no longer describes the kernel and is reported as null.
 TRAFFIC = {
+    ("decode_split_kernel", "decode-bf16-b256-ctx1024-8192-h32-8"): {
+        "bytes": 4844590120, "source": "decode.hip",
+        "sha256": "3418e9720d115fe4854c31d3ac04f3a0bdc974d46f20d6525757db4113b7b29d"},
     ("decode_split_kernel", "decode-bf16-b64-ctx512-4096-h16-8"): {
         "bytes": 545456801, "source": "decode.hip",
         "sha256": "3418e9720d115fe4854c31d3ac04f3a0bdc974d46f20d6525757db4113b7b29d"},
@@ -391,15 +406,14 @@ def time_contiguous_prefill(d: Device, steps: int, torch, settle_s: float = 0.5)
         e1.record(stream)
     torch.cuda.synchronize()
     del flush, k, v
-    return mean([e0.elapsed_time(e1) for e0, e1 in evs])
+    return median([e0.elapsed_time(e1) for e0, e1 in evs])
 
 
-def measure(index: int, steps: int, warmup: int, torch, settle_s: float):
-    from workloads import config
-
-    t = time.perf_counter()
-    w = config(index)
-    log(f"workload {index} ({w.spec.name}) generated in {time.perf_counter() - t:.1f}s")
+def measure(w, steps: int, warmup: int, torch, settle_s: float):
+    """Event-timed store, attention launches and (decode) fused step of one
+    workload, MALL evicted before every step; medians over the timed steps,
+    plus the mean duration of the roofline kernel (the one rocprofv3's
+    average is compared with)."""
     d = Device(w, torch)
     d.check()
     store_ms, part_ms, wall = time_steps(d, steps, warmup, torch, settle_s)
@@ -407,10 +421,11 @@ def measure(index: int, steps: int, warmup: int, torch, settle_s: float):
     step_ms = [a + b for a, b in zip(store_ms, attn_ms)]
     r = {
         "w": w,
-        "store_ms": mean(store_ms),
-        "attn_ms": mean(attn_ms),
-        "part_ms": [mean(p) for p in part_ms],
-        "step_ms": mean(step_ms),
+        "store_ms": median(store_ms),
+        "attn_ms": median(attn_ms),
+        "part_ms": [median(p) for p in part_ms],
+        "part_mean_ms": [mean(p) for p in part_ms],
+        "step_ms": median(step_ms),
         "wall_s": wall,
     }
     kv = w.logical_kv_bytes()
@@ -419,14 +434,16 @@ def measure(index: int, steps: int, warmup: int, torch, settle_s: float):
          r["fused_step_graph_ms"]) = time_fused_step(d, steps, warmup, torch)
         attn_bytes = kv + w.qo_bytes()
         r["attn_bytes"] = attn_bytes
+        r["unique_attn_bytes"] = w.unique_kv_bytes() + w.qo_bytes()
         r["attn_gbs"] = attn_bytes / (r["attn_ms"] * 1e-3) / 1e9
-        r["unique_gbs"] = (w.unique_kv_bytes() + w.qo_bytes()) / (r["attn_ms"] * 1e-3) / 1e9
+        r["unique_gbs"] = r["unique_attn_bytes"] / (r["attn_ms"] * 1e-3) / 1e9
         # the partials kernel reads every context K/V row and q
         r["split_bytes"] = kv + w.qo_bytes() // 2
-        r["split_gbs"] = r["split_bytes"] / (r["part_ms"][0] * 1e-3) / 1e9
+        r["split_gbs"] = r["split_bytes"] / (r["part_mean_ms"][0] * 1e-3) / 1e9
     else:
         r["flops"] = w.prefill_flops()
         r["tflops"] = r["flops"] / (r["attn_ms"] * 1e-3) / 1e12
+        r["tflops_mean"] = r["flops"] / (r["part_mean_ms"][0] * 1e-3) / 1e12
         r["contiguous_ms"] = time_contiguous_prefill(d, max(5, steps // 2), torch)
         r["contiguous_tflops"] = r["flops"] / (r["contiguous_ms"] * 1e-3) / 1e12
         # prefill reads each unique cached K/V byte at least once
@@ -441,43 +458,124 @@ def measure(index: int, steps: int, warmup: int, torch, settle_s: float):
     return r
 
 
-def cpu_baseline(index: int, budget_s: float = 10.0):
-    """The CPU oracle, as it stands, on the same workload: store, then decode
-    of every sequence (one sequence at a time), repeated until ~budget_s."""
+def summary(r) -> dict:
+    """Per-workload line of ``extra``: times (medians) and the fraction of
+    the roofline each part reaches."""
+    w = r["w"]
+    e = {"step_ms": round(r["step_ms"], 4), "store_ms": round(r["store_ms"], 4),
+         "attn_ms": round(r["attn_ms"], 4)}
+    if w.spec.mode == "prefill":
+        e.update(prefill_tflops=round(r["tflops"], 1),
+                 mfma_frac=round(r["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+                 prefill_tokens_per_s=round(w.num_tokens / (r["attn_ms"] * 1e-3), 1),
+                 contiguous_kv_ms=round(r["contiguous_ms"], 4),
+                 contiguous_kv_tflops=round(r["contiguous_tflops"], 1),
+                 contiguous_kv_mfma_frac=round(r["contiguous_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4))
+        return e
+    e.update(decode_gbs=round(r["attn_gbs"], 1),
+             decode_hbm_frac=round(r["attn_gbs"] / HBM_PEAK_GBS, 4),
+             partials_ms=round(r["part_ms"][0], 4),
+             partials_hbm_frac=round(r["split_bytes"] / (r["part_ms"][0] * 1e-3) / 1e9
+                                     / HBM_PEAK_GBS, 4),
+             merge_ms=round(r["part_ms"][1], 4) if len(r["part_ms"]) > 1 else None,
+             decode_tokens_per_s=round(w.batch / (r["attn_ms"] * 1e-3), 1),
+             fused_step_ms=round(r["fused_step_ms"], 4),
+             fused_step_gbs=round(r["fused_step_gbs"], 1),
+             fused_step_hbm_frac=round(r["fused_step_gbs"] / HBM_PEAK_GBS, 4),
+             fused_step_graph_ms=round(r["fused_step_graph_ms"], 4))
+    if r["unique_attn_bytes"] != r["attn_bytes"]:
+        e.update(decode_unique_gbs=round(r["unique_gbs"], 1),
+                 decode_unique_hbm_frac=round(r["unique_gbs"] / HBM_PEAK_GBS, 4))
+    return e
+
+
+def host_cores() -> int:
+    """CPU threads this process may use: its affinity set, capped by
+    OMP_NUM_THREADS when that is set (a GPU machine grants a share of its host)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    return min(n, int(omp)) if omp.isdigit() and int(omp) > 0 else n
+
+
+def cpu_baseline(w, budget_s: float = 8.0, cores: int = 0) -> dict:
+    """The CPU oracle, as it stands, on one workload, on ``cores`` host
+    threads.  Decode: the oracle's store, then its decode of every sequence,
+    sequences spread over a pool of ``cores`` threads (one BLAS thread each;
+    the oracle's per-head products are too small for BLAS threads to help),
+    whole passes repeated until ``budget_s``.  Prefill: the oracle's store,
+    then its prefill one sequence at a time with ``cores`` BLAS threads (the
+    products are large), sequences in order until ``budget_s`` -- a sample
+    whose size is stated.  Rates use the same algorithmic bytes and flops as
+    the GPU figures."""
     import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
     from threadpoolctl import threadpool_limits
 
     from oracle import ref
-    from workloads import bits_view, config
+    from workloads import bits_view
 
-    w = config(index)
+    cores = cores or host_cores()
     kb, vb = bits_view(w.k.contiguous()), bits_view(w.v.contiguous())
     kcb0, vcb0 = bits_view(w.k_cache), bits_view(w.v_cache)
     q = ref.widen(bits_view(w.q.contiguous()), w.dtype)
-    passes, nbytes, t0 = 0, 0, time.perf_counter()
-    with threadpool_limits(1):
-        while True:
-            kcb, vcb = ref.kv_store(kb, vb, kcb0, vcb0, w.slot_mapping, w.block_size)
-            for b in range(w.batch):
-                n = int(w.context_lens[b])
-                ids = w.block_tables[b, : ref.num_blocks(n, w.block_size)]
-                kc, vc = ref.widen(kcb[ids], w.dtype), ref.widen(vcb[ids], w.dtype)
-                ref.decode(q[b : b + 1], kc, vc, np.arange(len(ids), dtype=np.int32)[None],
-                           w.context_lens[b : b + 1], w.scale)
-            passes += 1
-            nbytes += w.store_bytes() + w.logical_kv_bytes() + w.qo_bytes()
-            if time.perf_counter() - t0 >= budget_s:
+    t0 = time.perf_counter()
+    kcb, vcb = ref.kv_store(kb, vb, kcb0, vcb0, w.slot_mapping, w.block_size)
+    store_s = time.perf_counter() - t0
+
+    def decode_one(b):
+        n = int(w.context_lens[b])
+        ids = w.block_tables[b, : ref.num_blocks(n, w.block_size)]
+        kc, vc = ref.widen(kcb[ids], w.dtype), ref.widen(vcb[ids], w.dtype)
+        ref.decode(q[b : b + 1], kc, vc, np.arange(len(ids), dtype=np.int32)[None],
+                   w.context_lens[b : b + 1], w.scale)
+
+    if w.spec.mode == "decode":
+        passes, t1 = 0, time.perf_counter()
+        with threadpool_limits(1), ThreadPoolExecutor(cores) as ex:
+            while True:
+                list(ex.map(decode_one, range(w.batch)))
+                passes += 1
+                if time.perf_counter() - t1 >= budget_s:
+                    break
+        dt = time.perf_counter() - t1
+        nbytes = w.logical_kv_bytes() + w.qo_bytes()
+        total_s = store_s + dt / passes  # one step: the store, then one decode pass
+        return {
+            "value": round((w.store_bytes() + nbytes) / total_s / 1e9, 4),
+            "unit": "GB/s",
+            "cores": cores,
+            "kind": "oracle",
+            "sample": f"whole workload: oracle store ({store_s:.2f} s) + decode of all {w.batch} "
+                      f"sequences, {passes} pass(es) in {dt:.1f} s on a pool of {cores} "
+                      f"threads, numpy fp64; value = step bytes / (store + one pass)",
+            "decode_gbs": round(nbytes / (dt / passes) / 1e9, 4),
+            "tokens_per_s": round(passes * w.batch / dt, 2),
+        }
+    kc, vc = ref.widen(kcb, w.dtype), ref.widen(vcb, w.dtype)
+    done, flops, rows, t1 = 0, 0, 0, time.perf_counter()
+    with threadpool_limits(cores):
+        for b in range(w.batch):
+            lo, hi = int(w.cu_seqlens_q[b]), int(w.cu_seqlens_q[b + 1])
+            ref.prefill(q[lo:hi], kc, vc, np.array([0, hi - lo], dtype=np.int32),
+                        w.context_lens[b : b + 1], w.block_tables[b : b + 1], w.scale)
+            nk, nq = int(w.context_lens[b]), hi - lo
+            flops += 4 * w.head_dim * w.num_q_heads * (nq * (nk - nq + 1) + nq * (nq - 1) // 2)
+            rows += nq
+            done += 1
+            if time.perf_counter() - t1 >= budget_s:
                 break
-    dt = time.perf_counter() - t0
+    dt = time.perf_counter() - t1
     return {
-        "value": round(nbytes / dt / 1e9, 4),
-        "unit": "GB/s",
-        "cores": 1,
+        "value": round(flops / dt / 1e9, 3),
+        "unit": "GFLOP/s",
+        "cores": cores,
         "kind": "oracle",
-        "sample": f"whole workload (store + decode of all {w.batch} sequences, numpy fp64, "
-                  f"one BLAS thread), {passes} pass(es) in {dt:.1f}s; host has "
-                  f"{os.cpu_count()} cpus",
-        "tokens_per_s": round(passes * w.batch / dt, 2),
+        "sample": f"oracle store of the whole workload ({store_s:.2f} s, not in the rate), "
+                  f"then prefill of the first {done} of {w.batch} sequences ({rows} of "
+                  f"{w.num_tokens} query rows, {flops / w.prefill_flops():.1%} of the flops) "
+                  f"in {dt:.1f} s with {cores} BLAS threads, numpy fp64",
+        "prefill_tokens_per_s": round(rows / dt, 2),
     }
 
 
@@ -504,7 +602,7 @@ def time_block_sizes(torch, steps: int = 10, warmup: int = 3) -> dict:
             d = Device(w, torch)
             d.check()
             _, part_ms, _ = time_steps(d, steps, warmup, torch, 0.3)
-            attn_ms = mean([sum(x) for x in zip(*part_ms)])
+            attn_ms = median([sum(x) for x in zip(*part_ms)])
             blocks = int((-(-w.context_lens.astype(np.int64) // B)).sum())
             e = {"attn_ms": round(attn_ms, 4),
                  "fragmentation": round(1 - float(w.context_lens.sum()) / (blocks * B), 4)}
@@ -632,9 +730,11 @@ def main() -> int:
     ap.add_argument("--settle", type=float, default=1.0,
                     help="seconds of back-to-back untimed steps before the warm-up steps, "
                          "so the GPU reaches its steady clocks")
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
+    ap.add_argument("--cpu-budget", type=float, default=8.0,
+                    help="seconds of oracle work per workload for the CPU baselines")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain copies of a known size (for HBM counters)")
     args = ap.parse_args()
@@ -654,40 +754,35 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     import paged_kv_cache_325_amd as pkv
+    from workloads import config
 
     pkv.load_library()  # fails loudly if the HIP library is missing
     if args.copy_calibration:
         copy_calibration(torch)
 
-    head = measure(args.workload, args.steps, args.warmup, torch, args.settle)
+    workloads = {}
+
+    def workload(i):
+        if i not in workloads:
+            t = time.perf_counter()
+            workloads[i] = config(i)
+            log(f"workload {i} ({workloads[i].spec.name}) generated in "
+                f"{time.perf_counter() - t:.1f}s")
+        return workloads[i]
+
+    head = measure(workload(args.workload), args.steps, args.warmup, torch, args.settle)
     w = head["w"]
-    log(f"headline: step {head['step_ms']:.4f} ms, decode {head['attn_ms']:.4f} ms, "
-        f"store {head['store_ms']:.4f} ms")
+    log(f"headline: {summary(head)}")
 
     extra = {}
     if not args.no_extra:
         for idx in (1, 2, 3, 4, 5):
             if idx == args.workload:
                 continue
-            r = measure(idx, max(3, args.steps // 2), max(1, args.warmup // 2), torch,
+            r = measure(workload(idx), max(3, args.steps // 2), max(1, args.warmup // 2), torch,
                         args.settle / 2)
-            e = {"step_ms": round(r["step_ms"], 4), "store_ms": round(r["store_ms"], 4),
-                 "attn_ms": round(r["attn_ms"], 4)}
-            if "tflops" in r:
-                e.update(prefill_tflops=round(r["tflops"], 1),
-                         mfma_frac=round(r["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
-                         prefill_tokens_per_s=round(r["w"].num_tokens / (r["attn_ms"] * 1e-3), 1),
-                         contiguous_kv_ms=round(r["contiguous_ms"], 4),
-                         contiguous_kv_tflops=round(r["contiguous_tflops"], 1))
-            else:
-                e.update(decode_gbs=round(r["attn_gbs"], 1),
-                         hbm_frac=round(r["attn_gbs"] / HBM_PEAK_GBS, 4),
-                         decode_unique_gbs=round(r["unique_gbs"], 1),
-                         decode_tokens_per_s=round(r["w"].batch / (r["attn_ms"] * 1e-3), 1),
-                         fused_step_ms=round(r["fused_step_ms"], 4),
-                         fused_step_graph_ms=round(r["fused_step_graph_ms"], 4))
-            extra[r["w"].spec.name] = e
-            log(f"workload {idx}: {e}")
+            extra[r["w"].spec.name] = summary(r)
+            log(f"workload {idx}: {extra[r['w'].spec.name]}")
 
     if w.spec.mode == "decode":
         roof = {"bound": "hbm", "achieved": round(head["split_gbs"], 2), "peak": HBM_PEAK_GBS,
@@ -695,21 +790,22 @@ def main() -> int:
                 "traffic": traffic_for("decode_split_kernel", w.spec.name),
                 "kernel": "decode_split_kernel (pkv_paged_decode_partials)",
                 "bytes_per_launch": head["split_bytes"],
-                "mean_launch_ms": round(head["part_ms"][0], 5),
-                "merge_kernel_mean_ms": round(head["part_ms"][1], 5)}
+                "mean_launch_ms": round(head["part_mean_ms"][0], 5),
+                "median_launch_ms": round(head["part_ms"][0], 5),
+                "merge_kernel_median_ms": round(head["part_ms"][1], 5)}
     else:
-        roof = {"bound": "mfma", "achieved": round(head["tflops"], 2),
+        roof = {"bound": "mfma", "achieved": round(head["tflops_mean"], 2),
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(head["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+                "frac": round(head["tflops_mean"] / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": traffic_for("prefill_kernel", w.spec.name),
                 "kernel": "prefill_kernel", "flops_per_launch": head["flops"],
-                "mean_launch_ms": round(head["attn_ms"], 5)}
+                "mean_launch_ms": round(head["part_mean_ms"][0], 5),
+                "median_launch_ms": round(head["part_ms"][0], 5)}
 
     if not args.no_extra:
         log("timing a 28-layer decode step, eager and from a captured graph")
-        from workloads import config
-        stacks = [config(1)] + [decode_batch_bucket(nb) for nb in (1, 4, 16)] + [config(2)]
-        extra["decode-step-28-layers"] = [time_layer_stack(torch, w) for w in stacks]
+        stacks = [workload(1)] + [decode_batch_bucket(nb) for nb in (1, 4, 16)] + [workload(2)]
+        extra["decode-step-28-layers"] = [time_layer_stack(torch, x) for x in stacks]
         log(f"28-layer decode step: {extra['decode-step-28-layers']}")
         log("timing other cache block sizes")
         extra["block-size-study"] = time_block_sizes(torch)
@@ -717,10 +813,19 @@ def main() -> int:
         extra["block-manager-host"] = time_block_manager()
 
     cpu = None
-    if not args.no_cpu and w.spec.mode == "decode":
-        log("timing the CPU oracle")
-        cpu = cpu_baseline(args.workload)
+    if not args.no_cpu:
+        cores = host_cores()
+        log(f"timing the CPU oracle on {cores} host threads")
+        cpu = cpu_baseline(w, args.cpu_budget, cores)
+        log(f"oracle, {w.spec.name}: {cpu}")
         if not args.no_extra:
+            per = {}
+            for idx in (1, 2, 3, 4, 5):
+                if idx != args.workload:
+                    x = workload(idx)
+                    per[x.spec.name] = cpu_baseline(x, args.cpu_budget, cores)
+                    log(f"oracle, {x.spec.name}: {per[x.spec.name]}")
+            cpu["per_workload"] = per
             cpu["block_manager"] = block_manager_oracle()
 
     # The headline step: for decode the library's one-call step
@@ -754,18 +859,17 @@ def main() -> int:
             "stored_tokens": int((w.slot_mapping >= 0).sum()),
             "seed": w.spec.seed,
         },
-        "decode_gbs": round(head.get("attn_gbs", 0.0), 2),
-        "decode_tokens_per_s": round(w.batch / (head["attn_ms"] * 1e-3), 1),
-        "step_tokens_per_s": round(w.batch / (step_ms * 1e-3), 1),
         "step_path": ("pkv_paged_decode_step (kv_store fused into the decode)" if fused
                       else "pkv_kv_store + attention call"),
-        "hbm_frac": round(head.get("attn_gbs", 0.0) / HBM_PEAK_GBS, 4),
+        "step_tokens_per_s": round(w.batch / (step_ms * 1e-3), 1) if fused else None,
+        "headline": summary(head),
         "separate_calls": {"step_ms": round(head["step_ms"], 5),
                            "step_gbs": round(head["step_gbs"], 2),
                            "store_ms": round(head["store_ms"], 5)},
         "step_graph_replay_ms": (round(head["fused_step_graph_ms"], 5) if fused else None),
-        "timing": "HIP events on the kernels' stream, mean over the timed steps; 1 GiB "
-                  "read-only MALL eviction before every step (outside the events); "
+        "timing": "HIP events on the kernels' stream; medians over the timed steps (the "
+                  "roofline kernel: mean, as rocprofv3 averages); 1 GiB read-only MALL eviction "
+                  "before every step (outside the events); "
                   f"{args.settle:g} s of untimed back-to-back steps before the warm-up",
         "wall_s_timed_region": round(wall_s, 3),
         "roofline": roof,

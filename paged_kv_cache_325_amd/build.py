@@ -1,6 +1,6 @@
 """Compile libpkv.so (the HIP kernels and their C ABI) for gfx950, in-tree.
 
-    python -m paged_kv_cache_325_amd.build [--debug]
+    python -m paged_kv_cache_325_amd.build [-v]
 
 Each ``csrc/*.hip`` file (hipcc) and each host-only ``csrc/*.cpp`` file (g++)
 is compiled to an object under ``_build/`` in parallel, then linked into
@@ -46,7 +46,7 @@ def gxx() -> str:
 PER_FILE_FLAGS = {"prefill.hip": ["-fno-honor-nans"]}
 
 
-def _flags(debug: bool):
+def _flags():
     f = [
         f"--offload-arch={ARCH}",
         "-std=c++17",
@@ -57,16 +57,14 @@ def _flags(debug: bool):
         f"-I{INCLUDE}",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     ]
-    if debug:
-        f += ["-DPKV_DEBUG_CHECKS=1"]
     return f
 
 
-def build(debug: bool = False, verbose: bool = False) -> str:
+def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     cc = hipcc()
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    flags = _flags(debug)
+    flags = _flags()
 
     def compile_one(src):
         obj = os.path.join(BUILD_DIR, os.path.basename(src)[:-4] + ".o")
@@ -102,4 +100,4 @@ def build(debug: bool = False, verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(debug="--debug" in sys.argv, verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv))
