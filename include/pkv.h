@@ -242,6 +242,40 @@ pkv_status pkv_paged_decode_step(
     int32_t block_size, int64_t num_blocks, float scale, int32_t num_splits,
     void* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * pkv_paged_decode_step_noalloc -- pkv_paged_decode_step for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, checks and
+ * results (bitwise) as pkv_paged_decode_step with the same split plan, but no
+ * workspace: the split-K partials go to a fixed scratch array of
+ * PKV_NOALLOC_SCRATCH_BYTES (32 MiB) that the library holds on each GPU it
+ * runs on, from the first call on that GPU until the process ends.  The
+ * caller still passes inputs and outputs.  Nothing is allocated, freed or
+ * memset per call.
+ *
+ *   PKV_ERR_WORKSPACE  the plan's partials need more than
+ *                      PKV_NOALLOC_SCRATCH_BYTES (compare
+ *                      pkv_paged_decode_workspace_bytes beforehand; fewer
+ *                      splits or a smaller batch fit); checked before any
+ *                      HIP call
+ *   PKV_ERR_HIP        the scratch's device address could not be found
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's contents: calls that may overlap on one GPU (different streams,
+ * threads or processes' graphs replayed concurrently) race and must be
+ * serialised by the caller.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+pkv_status pkv_paged_decode_step_noalloc(
+    pkv_dtype dtype, const void* q, int64_t q_token_stride, const void* k_new,
+    int64_t k_new_token_stride, const void* v_new, int64_t v_new_token_stride,
+    const int32_t* slot_mapping, void* k_cache, void* v_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, int32_t max_context_len, int32_t batch,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int64_t num_blocks, float scale, int32_t num_splits,
+    void* out, void* stream);
+
 pkv_status pkv_paged_decode_merge(pkv_dtype dtype, const int32_t* context_lens,
                                   int32_t max_context_len, int32_t batch,
                                   int32_t num_q_heads, int32_t num_kv_heads,

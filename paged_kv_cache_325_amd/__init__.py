@@ -8,7 +8,8 @@ missing or a tensor is not on the GPU, the call raises.
 
 Names follow the C ABI: ``pkv_kv_store``, ``pkv_paged_decode`` (and its two
 halves ``pkv_paged_decode_partials`` / ``pkv_paged_decode_merge``),
-``pkv_paged_decode_step`` (store fused into decode), ``pkv_paged_decode_workspace_bytes``,
+``pkv_paged_decode_step`` (store fused into decode), ``pkv_paged_decode_step_noalloc``
+(the same without a workspace), ``pkv_paged_decode_workspace_bytes``,
 ``pkv_paged_decode_split_tokens``, ``pkv_paged_prefill_workspace_bytes``,
 ``pkv_paged_prefill_varlen``, ``pkv_prefill_varlen`` (contiguous k/v, no cache),
 ``pkv_kv_block_bytes``, ``pkv_last_error``.
@@ -26,7 +27,7 @@ __all__ = [
     "PKV_OK", "PKV_ERR_INVALID", "PKV_ERR_UNSUPPORTED", "PKV_ERR_WORKSPACE", "PKV_ERR_HIP",
     "PKV_FP32", "PKV_BF16", "PkvError", "lib_path", "load_library",
     "pkv_kv_store", "pkv_paged_decode", "pkv_paged_decode_partials", "pkv_paged_decode_merge",
-    "pkv_paged_decode_step",
+    "pkv_paged_decode_step", "pkv_paged_decode_step_noalloc", "PKV_NOALLOC_SCRATCH_BYTES",
     "pkv_paged_decode_workspace_bytes",
     "pkv_paged_decode_split_tokens", "pkv_paged_prefill_varlen",
     "pkv_paged_prefill_workspace_bytes", "pkv_prefill_varlen", "pkv_kv_block_bytes",
@@ -35,6 +36,7 @@ __all__ = [
 
 PKV_OK, PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP = range(5)
 PKV_FP32, PKV_BF16 = 0, 1
+PKV_NOALLOC_SCRATCH_BYTES = 32 << 20  # include/pkv.h
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -76,6 +78,11 @@ def load_library() -> ctypes.CDLL:
     lib.pkv_paged_decode_step.argtypes = [c_i32, c_p, c_i64, c_p, c_i64, c_p, c_i64, c_p, c_p, c_p,
                                           c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                           c_i64, c_f, c_i32, c_p, c_p, ctypes.c_size_t, c_p]
+    lib.pkv_paged_decode_step_noalloc.restype = c_i32
+    lib.pkv_paged_decode_step_noalloc.argtypes = [c_i32, c_p, c_i64, c_p, c_i64, c_p, c_i64, c_p,
+                                                  c_p, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32,
+                                                  c_i32, c_i32, c_i32, c_i64, c_f, c_i32, c_p,
+                                                  c_p]
     lib.pkv_paged_decode_merge.restype = c_i32
     lib.pkv_paged_decode_merge.argtypes = [c_i32, c_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                            c_i32, c_p, c_p, ctypes.c_size_t, c_p]
@@ -238,16 +245,9 @@ def pkv_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
                         max_context_len, scale, out, workspace, num_splits, stream)[0]
 
 
-def pkv_paged_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
-                          slot_mapping: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-                          block_tables: torch.Tensor, context_lens: torch.Tensor,
-                          max_context_len: int, scale: float, out: Optional[torch.Tensor] = None,
-                          workspace: Optional[torch.Tensor] = None, num_splits: int = 0,
-                          stream=None) -> torch.Tensor:
-    """One decode step: store k_new/v_new ([batch, Hkv, D]) at slot_mapping
-    and decode q ([batch, Hq, D]) over the cache, in one call (see
-    pkv_paged_decode_step in include/pkv.h for the decode-step invariant)."""
-    lib = load_library()
+def _step_args(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables, context_lens,
+               out):
+    """Checked pointers and sizes of a decode step (shared by both forms)."""
     for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"),
                  (v_cache, "v_cache")):
         _gpu(t, n)
@@ -268,20 +268,56 @@ def pkv_paged_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Ten
             or block_tables.shape[0] != batch):
         raise ValueError("q, k_new, v_new, slot_mapping, context_lens and block_tables must "
                          "agree on the batch")
-    if out is None:
-        out = torch.empty((batch, hq, d), dtype=q.dtype, device=q.device)
     _gpu(out, "out")
     if out.shape != (batch, hq, d) or not out.is_contiguous() or out.dtype != q.dtype:
         raise ValueError("out must be a contiguous [batch, Hq, D] tensor of q's dtype")
+    return (batch, hq, hkv, d, bs, nblk,
+            [_dtype_code(q), _ptr(q), qs, _ptr(k_new), ks, _ptr(v_new), vs, _ptr(slot_mapping),
+             _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), int(block_tables.shape[1]),
+             _ptr(context_lens)])
+
+
+def pkv_paged_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                          slot_mapping: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          block_tables: torch.Tensor, context_lens: torch.Tensor,
+                          max_context_len: int, scale: float, out: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None, num_splits: int = 0,
+                          stream=None) -> torch.Tensor:
+    """One decode step: store k_new/v_new ([batch, Hkv, D]) at slot_mapping
+    and decode q ([batch, Hq, D]) over the cache, in one call (see
+    pkv_paged_decode_step in include/pkv.h for the decode-step invariant)."""
+    lib = load_library()
+    if out is None:
+        _gpu(q, "q")
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    batch, hq, hkv, d, bs, nblk, head = _step_args(q, k_new, v_new, slot_mapping, k_cache,
+                                                   v_cache, block_tables, context_lens, out)
     need = pkv_paged_decode_workspace_bytes(batch, hq, hkv, d, max_context_len, bs, num_splits)
     if workspace is None and need > 0:
         workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.pkv_paged_decode_step(
-        _dtype_code(q), _ptr(q), qs, _ptr(k_new), ks, _ptr(v_new), vs, _ptr(slot_mapping),
-        _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), int(block_tables.shape[1]),
-        _ptr(context_lens), int(max_context_len), batch, hq, hkv, d, bs, nblk, float(scale),
+        *head, int(max_context_len), batch, hq, hkv, d, bs, nblk, float(scale),
         int(num_splits), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def pkv_paged_decode_step_noalloc(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                                  slot_mapping: torch.Tensor, k_cache: torch.Tensor,
+                                  v_cache: torch.Tensor, block_tables: torch.Tensor,
+                                  context_lens: torch.Tensor, max_context_len: int, scale: float,
+                                  out: torch.Tensor, num_splits: int = 0,
+                                  stream=None) -> torch.Tensor:
+    """pkv_paged_decode_step without a workspace, allocating nothing: the
+    split-K partials go to the library's fixed per-GPU scratch of
+    PKV_NOALLOC_SCRATCH_BYTES.  ``out`` must be given.  Calls that overlap on
+    one GPU race on the scratch."""
+    lib = load_library()
+    batch, hq, hkv, d, bs, nblk, head = _step_args(q, k_new, v_new, slot_mapping, k_cache,
+                                                   v_cache, block_tables, context_lens, out)
+    _check(lib.pkv_paged_decode_step_noalloc(
+        *head, int(max_context_len), batch, hq, hkv, d, bs, nblk, float(scale),
+        int(num_splits), _ptr(out), _stream(stream)))
     return out
 
 

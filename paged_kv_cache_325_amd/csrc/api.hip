@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 #include <string>
 
 #include "pkv.h"
@@ -152,6 +154,44 @@ namespace {
 
 enum DecodeParts { kSplitOnly = 1, kMergeOnly = 2, kSplitAndMerge = 3 };
 
+// ---- fixed scratch of pkv_paged_decode_step_noalloc ------------------------
+// For callers that cannot allocate device memory, the split-K partials of the
+// no-allocation decode step live in this array, one copy per GPU, allocated
+// with the library's code object and held until the process ends.  In host
+// code `scratch` names a host-side stand-in, not the device array: its device
+// address is looked up once per device (hipGetSymbolAddress, with that device
+// current) and only that address is ever handed to a kernel.  Every call on a
+// GPU shares its copy, so calls that overlap on one GPU race.  The partials
+// need no initialisation (each is written before the merge reads it).
+static __device__ __align__(256) float scratch[PKV_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+pkv_status scratch_for_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PKV_ERR_UNSUPPORTED, "device %d: the fixed scratch serves devices 0..%d", dev,
+                kMaxDevices - 1);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+      if (!p || ((uintptr_t)p & 255u) != 0)
+        return fail(PKV_ERR_HIP, "the fixed scratch has no 256-byte aligned device address");
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return PKV_OK;
+}
+
 // This step's K/V rows for the fused store of pkv_paged_decode_step.
 struct FusedStore {
   const void* k_new;
@@ -167,7 +207,7 @@ pkv_status check_decode_common(pkv_dtype dtype, int32_t batch, int32_t num_q_hea
                                int32_t max_context_len, int32_t num_splits,
                                const int32_t* context_lens, const void* out,
                                const void* workspace, size_t workspace_bytes,
-                               pkv::DecodePlan* plan) {
+                               pkv::DecodePlan* plan, bool use_scratch) {
   if (elem_bytes(dtype) == 0) return fail(PKV_ERR_INVALID, "unknown dtype %d", (int)dtype);
   if (batch < 0) return fail(PKV_ERR_INVALID, "batch (%d) < 0", batch);
   if (max_context_len < 0 || num_splits < 0)
@@ -184,6 +224,15 @@ pkv_status check_decode_common(pkv_dtype dtype, int32_t batch, int32_t num_q_hea
   if (!pkv::plan_decode(batch, num_q_heads, num_kv_heads, max_context_len, num_splits,
                         block_size, plan))
     return fail(PKV_ERR_UNSUPPORTED, "no decode plan for these arguments");
+  if (use_scratch) {
+    if (plan->workspace_bytes > (size_t)PKV_NOALLOC_SCRATCH_BYTES)
+      return fail(PKV_ERR_WORKSPACE,
+                  "this decode step needs %zu bytes of split-K partials, more than the %zu "
+                  "bytes of the library's fixed scratch; use pkv_paged_decode_step with a "
+                  "caller workspace (or fewer splits)",
+                  plan->workspace_bytes, (size_t)PKV_NOALLOC_SCRATCH_BYTES);
+    return PKV_OK;
+  }
   if (workspace_bytes < plan->workspace_bytes || (plan->workspace_bytes && !workspace))
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
                 workspace ? workspace_bytes : (size_t)0, plan->workspace_bytes);
@@ -199,7 +248,7 @@ pkv_status decode_parts(int parts, pkv_dtype dtype, const void* q, int64_t q_tok
                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                         int64_t num_blocks, float scale, int32_t num_splits, void* out,
                         void* workspace, size_t workspace_bytes, void* stream,
-                        const FusedStore* fs = nullptr) {
+                        const FusedStore* fs = nullptr, bool use_scratch = false) {
   const int eb = elem_bytes(dtype);
   if (eb == 0) return fail(PKV_ERR_INVALID, "unknown dtype %d", (int)dtype);
   pkv_status st = check_geometry(num_q_heads, num_kv_heads, head_dim, block_size);
@@ -214,7 +263,7 @@ pkv_status decode_parts(int parts, pkv_dtype dtype, const void* q, int64_t q_tok
   pkv::DecodePlan plan;
   st = check_decode_common(dtype, batch, num_q_heads, num_kv_heads, head_dim,
                                       block_size, max_context_len, num_splits, context_lens, out,
-                                      workspace, workspace_bytes, &plan);
+                                      workspace, workspace_bytes, &plan, use_scratch);
   if (st != PKV_OK || batch == 0) return st;
   if (parts & kSplitOnly) {
     if (!q) return fail(PKV_ERR_INVALID, "null q with batch = %d", batch);
@@ -257,6 +306,12 @@ pkv_status decode_parts(int parts, pkv_dtype dtype, const void* q, int64_t q_tok
   l.scale = scale;
   l.out = out;
   l.workspace = plan.workspace_bytes ? (float*)workspace : nullptr;
+  if (use_scratch && plan.workspace_bytes) {
+    // every host argument has been checked: the first HIP call of this path
+    void* ptr = nullptr;
+    if ((st = scratch_for_current_device(&ptr)) != PKV_OK) return st;
+    l.workspace = (float*)ptr;
+  }
   if (fs) {
     l.k_new = fs->k_new;
     l.k_new_stride = fs->k_stride;
@@ -307,6 +362,24 @@ pkv_status pkv_paged_decode_step(pkv_dtype dtype, const void* q, int64_t q_token
                       max_blocks_per_seq, context_lens, max_context_len, batch, num_q_heads,
                       num_kv_heads, head_dim, block_size, num_blocks, scale, num_splits, out,
                       workspace, workspace_bytes, stream, &fs);
+}
+
+pkv_status pkv_paged_decode_step_noalloc(pkv_dtype dtype, const void* q, int64_t q_token_stride,
+                                         const void* k_new, int64_t k_new_token_stride,
+                                         const void* v_new, int64_t v_new_token_stride,
+                                         const int32_t* slot_mapping, void* k_cache,
+                                         void* v_cache, const int32_t* block_tables,
+                                         int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                         int32_t max_context_len, int32_t batch,
+                                         int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t block_size,
+                                         int64_t num_blocks, float scale, int32_t num_splits,
+                                         void* out, void* stream) {
+  const FusedStore fs{k_new, k_new_token_stride, v_new, v_new_token_stride, slot_mapping};
+  return decode_parts(kSplitAndMerge, dtype, q, q_token_stride, k_cache, v_cache, block_tables,
+                      max_blocks_per_seq, context_lens, max_context_len, batch, num_q_heads,
+                      num_kv_heads, head_dim, block_size, num_blocks, scale, num_splits, out,
+                      nullptr, 0, stream, &fs, /*use_scratch=*/true);
 }
 
 pkv_status pkv_paged_decode_partials(pkv_dtype dtype, const void* q, int64_t q_token_stride,

@@ -114,6 +114,28 @@ def test_decode_step_errors():
     assert "k_new" in (_step(kn=None) and pkv.pkv_last_error())
 
 
+def test_noalloc_step_rejects_plans_beyond_its_scratch():
+    """The no-allocation decode step refuses a plan whose partials exceed the
+    fixed scratch, and a non-finite scale, before any HIP call."""
+    lib = pkv.load_library()
+
+    def call(batch, maxctx, splits):
+        return lib.pkv_paged_decode_step_noalloc(
+            BF16, FAKE, 32 * 128, FAKE, 8 * 128, FAKE, 8 * 128, FAKE, FAKE, FAKE, FAKE,
+            maxctx // 256, FAKE, maxctx, batch, 32, 8, 128, 256, 1 << 20, 0.088, splits, FAKE,
+            None)
+
+    need = pkv.pkv_paged_decode_workspace_bytes(4096, 32, 8, 128, 32768, 256, 0)
+    assert need > pkv.PKV_NOALLOC_SCRATCH_BYTES
+    assert call(4096, 32768, 0) == WORKSPACE
+    assert "scratch" in pkv.pkv_last_error()
+    assert call(0, 32768, 0) == OK  # empty batch: nothing to do
+    for bad in (float("nan"), float("inf")):
+        assert lib.pkv_paged_decode_step_noalloc(
+            BF16, FAKE, 32 * 128, FAKE, 8 * 128, FAKE, 8 * 128, FAKE, FAKE, FAKE, FAKE, 16, FAKE,
+            4096, 16, 32, 8, 128, 256, 1 << 20, bad, 0, FAKE, None) == INVALID
+
+
 def test_decode_errors():
     assert _decode(batch=0) == OK
     assert _decode(batch=-1) == INVALID

@@ -1,0 +1,57 @@
+"""GPU: pkv_paged_decode_step_noalloc (no workspace; split-K partials in the
+library's fixed per-GPU scratch) against pkv_paged_decode_step with a caller
+workspace, bitwise on outputs and both caches, on two calls in a row -- the
+second with a smaller input, so it runs on whatever the first left in the
+scratch -- and against the oracle."""
+
+from __future__ import annotations
+
+import pytest
+import torch
+
+import paged_kv_cache_325_amd as pkv
+from tests.gpu_helpers import announce, assert_close, check_inputs, to_device
+from tests.oracle_helpers import expected
+from workloads import Spec, build, config
+
+pytestmark = pytest.mark.gpu
+
+
+def _step_both_ways(w, num_splits):
+    hq, hkv = w.num_q_heads, w.num_kv_heads
+    need = pkv.pkv_paged_decode_workspace_bytes(w.batch, hq, hkv, 128, w.max_context_len,
+                                                w.block_size, num_splits)
+    assert 0 < need <= pkv.PKV_NOALLOC_SCRATCH_BYTES  # the plan splits: scratch in use
+    a, b = to_device(w), to_device(w)
+    check_inputs(a)
+    announce(f"{w.spec.name}: decode step with a caller workspace (splits {num_splits})")
+    want = pkv.pkv_paged_decode_step(a.q, a.k, a.v, a.slot_mapping, a.k_cache, a.v_cache,
+                                     a.block_tables, a.context_lens, w.max_context_len, w.scale,
+                                     num_splits=num_splits)
+    announce(f"{w.spec.name}: decode step without allocation (splits {num_splits})")
+    out = torch.full_like(want, float("nan"))
+    got = pkv.pkv_paged_decode_step_noalloc(b.q, b.k, b.v, b.slot_mapping, b.k_cache, b.v_cache,
+                                            b.block_tables, b.context_lens, w.max_context_len,
+                                            w.scale, out=out, num_splits=num_splits)
+    torch.cuda.synchronize()
+    assert got is out
+    bits = torch.int16 if w.dtype == "bf16" else torch.int32  # the caches hold NaN poison
+    assert torch.equal(want.view(bits), out.view(bits))
+    assert torch.equal(a.k_cache.view(bits), b.k_cache.view(bits))
+    assert torch.equal(a.v_cache.view(bits), b.v_cache.view(bits))
+    assert_close(out.double().cpu().numpy(), expected(w), w.spec.name)
+
+
+def test_noalloc_step_two_calls_second_smaller():
+    # first: the 64-sequence decode workload, automatic plan (16 splits of
+    # 256 keys, 8.5 MB of partials); second: 5 sequences, 4 requested splits
+    _step_both_ways(config(2), 0)
+    small = build(Spec("noalloc-small", "decode", "bf16", 16, 8, [3000, 17, 900, 1, 2049],
+                       [1] * 5, 9501))
+    _step_both_ways(small, 4)
+
+
+def test_noalloc_step_fp32_after_bf16():
+    # fp32 partials of another shape over the same scratch
+    w = build(Spec("noalloc-fp32", "decode", "fp32", 8, 2, [700, 1500, 3], [1] * 3, 9502))
+    _step_both_ways(w, 3)
