@@ -257,13 +257,9 @@ def test_decode_deterministic_and_permutation_bit_exact():
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
 
 
-def test_shared_prefix_equals_private_copies_bit_exact():
-    w = build([s for s in SMALL if s.name == "dec-bf16-shared"][0])
-    d = to_device(w)
-    check_inputs(d)
-    store(d)
-    announce("shared prefix: decode")
-    a = _decode_out(d)
+def _private_copies(w, d):
+    """The same logical K/V with every shared block duplicated into a block
+    of its own: (k_cache, v_cache, block_tables) on the GPU."""
     bt = w.block_tables.copy()
     extra = []
     nxt = w.num_blocks
@@ -276,7 +272,61 @@ def test_shared_prefix_equals_private_copies_bit_exact():
     idx = torch.tensor(extra, device="cuda", dtype=torch.long)
     kc2 = torch.cat([d.k_cache, d.k_cache[idx]]).contiguous()
     vc2 = torch.cat([d.v_cache, d.v_cache[idx]]).contiguous()
-    bt2 = torch.from_numpy(bt).cuda()
+    return kc2, vc2, torch.from_numpy(bt).cuda()
+
+
+# Sequences 0/1 share 6 blocks, 2/3 one block (sequence 3's only full one),
+# 4/5 share none, 6/7 share 3 of which 7 uses 2, and 8 shares with nobody;
+# shared runs start on and off split boundaries under the split plans below.
+PAIR_CTX = [3000, 2500, 600, 257, 900, 900, 1800, 700, 1500]
+PAIR_GROUPS = [0, 0, 1, 1, -1, -1, 2, 2, -1]
+PAIR_SHARED = [6, 6, 1, 1, 0, 0, 3, 2, 0]
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3, 16])
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (4, 2), (2, 2), (8, 1)],
+                         ids=["g4", "g2", "g1", "g8"])
+def test_pairs_sharing_blocks_bitwise_equal_private(hq, hkv, splits):
+    """Prefix-shared blocks give identical outputs: decode and the fused step
+    over shared prefix blocks are bitwise equal to the same K/V in private
+    blocks (where no two tables match), for every GQA group size and several
+    split plans, and match the oracle."""
+    w = build(Spec(f"pairs-h{hq}-{hkv}", "decode", "bf16", hq, hkv, PAIR_CTX, [1] * 9,
+                   9601 + hq + hkv, share_group=PAIR_GROUPS, shared_blocks=PAIR_SHARED))
+    d = to_device(w)
+    check_inputs(d)
+    kc2, vc2, bt2 = _private_copies(w, d)
+    announce(f"pairs h{hq}/{hkv} splits {splits}: fused step, shared and private")
+    k_pre, v_pre = d.k_cache.clone(), d.v_cache.clone()
+    out_step = pkv.pkv_paged_decode_step(d.q, d.k, d.v, d.slot_mapping, d.k_cache, d.v_cache,
+                                         d.block_tables, d.context_lens, w.max_context_len,
+                                         w.scale, num_splits=splits)
+    kc3, vc3, _ = _private_copies(w, dataclasses.replace(d, k_cache=k_pre, v_cache=v_pre))
+    out_step2 = pkv.pkv_paged_decode_step(d.q, d.k, d.v, d.slot_mapping, kc3, vc3, bt2,
+                                          d.context_lens, w.max_context_len, w.scale,
+                                          num_splits=splits)
+    announce(f"pairs h{hq}/{hkv} splits {splits}: decode, shared and private")
+    store(d)
+    kc2, vc2, _ = _private_copies(w, d)
+    a = pkv.pkv_paged_decode(d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens,
+                             w.max_context_len, w.scale, num_splits=splits)
+    c = pkv.pkv_paged_decode(d.q, kc2, vc2, bt2, d.context_lens, w.max_context_len, w.scale,
+                             num_splits=splits)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+    assert torch.equal(out_step.view(torch.int16), a.view(torch.int16))
+    assert torch.equal(out_step2.view(torch.int16), a.view(torch.int16))
+    assert_close(a.double().cpu().numpy(), expected(w), w.spec.name)
+
+
+def test_shared_prefix_equals_private_copies_bit_exact():
+    w = build([s for s in SMALL if s.name == "dec-bf16-shared"][0])
+    d = to_device(w)
+    check_inputs(d)
+    store(d)
+    announce("shared prefix: decode")
+    a = _decode_out(d)
+    kc2, vc2, bt2 = _private_copies(w, d)
     announce("shared prefix: decode on private copies")
     c = pkv.pkv_paged_decode(d.q, kc2, vc2, bt2, d.context_lens, w.max_context_len, w.scale)
     torch.cuda.synchronize()
