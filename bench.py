@@ -338,9 +338,15 @@ TRAFFIC = {
     ("decode_split_kernel", "decode-bf16-b64-ctx512-4096-h16-8"): {
         "bytes": 545456801, "source": "decode.hip",
         "sha256": "3418e9720d115fe4854c31d3ac04f3a0bdc974d46f20d6525757db4113b7b29d"},
+    ("decode_split_kernel", "decode-bf16-b16-lognormal8192-shared4096-h32-8"): {
+        "bytes": 620467092, "source": "decode.hip",
+        "sha256": "3418e9720d115fe4854c31d3ac04f3a0bdc974d46f20d6525757db4113b7b29d"},
+    ("decode_split_kernel", "decode-fp32-4seq"): {
+        "bytes": 9206271, "source": "decode.hip",
+        "sha256": "3418e9720d115fe4854c31d3ac04f3a0bdc974d46f20d6525757db4113b7b29d"},
     ("prefill_kernel", "prefill-bf16-8seq-L1024-4096-prefix512-h32-8"): {
-        "bytes": 2097328039, "source": "prefill.hip",
-        "sha256": "3a3c35d5ed588efe286e2119aa30e940e3e4db80f71c4d81cbec4b2e863ec19f"},
+        "bytes": 2060125220, "source": "prefill.hip",
+        "sha256": "7f34c5428050279b92dee9a81fc4a5ea63ce234783d2aaf20844a8560753eb2a"},
 }
 
 
@@ -465,6 +471,7 @@ def summary(r) -> dict:
     e = {"step_ms": round(r["step_ms"], 4), "store_ms": round(r["store_ms"], 4),
          "attn_ms": round(r["attn_ms"], 4)}
     if w.spec.mode == "prefill":
+        e.update(hbm_traffic_bytes=traffic_for("prefill_kernel", w.spec.name))
         e.update(prefill_tflops=round(r["tflops"], 1),
                  mfma_frac=round(r["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
                  prefill_tokens_per_s=round(w.num_tokens / (r["attn_ms"] * 1e-3), 1),
@@ -472,6 +479,7 @@ def summary(r) -> dict:
                  contiguous_kv_tflops=round(r["contiguous_tflops"], 1),
                  contiguous_kv_mfma_frac=round(r["contiguous_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4))
         return e
+    e.update(partials_hbm_traffic_bytes=traffic_for("decode_split_kernel", w.spec.name))
     e.update(decode_gbs=round(r["attn_gbs"], 1),
              decode_hbm_frac=round(r["attn_gbs"] / HBM_PEAK_GBS, 4),
              partials_ms=round(r["part_ms"][0], 4),
