@@ -345,8 +345,8 @@ TRAFFIC = {
         "bytes": 9206271, "source": "decode.hip",
         "sha256": "3418e9720d115fe4854c31d3ac04f3a0bdc974d46f20d6525757db4113b7b29d"},
     ("prefill_kernel", "prefill-bf16-8seq-L1024-4096-prefix512-h32-8"): {
-        "bytes": 2060125220, "source": "prefill.hip",
-        "sha256": "7f34c5428050279b92dee9a81fc4a5ea63ce234783d2aaf20844a8560753eb2a"},
+        "bytes": 2076887192, "source": "prefill.hip",
+        "sha256": "80c6d337d028d260fd2ce99e992ec11b6f6be0e48a6f9b9dfa94afc69e46f88e"},
 }
 
 
