@@ -309,7 +309,11 @@ pkv_status pkv_paged_decode_merge(pkv_dtype dtype, const int32_t* context_lens,
  *                  the persistent kernel.  It must be zero-filled before its
  *                  first use; every call leaves it zero again when its
  *                  kernel ends, so one fill at allocation suffices.  Calls
- *                  that may run concurrently need distinct workspaces.
+ *                  that may run concurrently need distinct workspaces.  A
+ *                  workspace that was not zeroed gives wrong (possibly
+ *                  unwritten) output rows but no access outside the
+ *                  problem: work-item ids outside the item range are
+ *                  treated as an exhausted queue.
  * total_q = cu_seqlens_q[batch] is not passed; rows outside the ranges are
  * neither read nor written.  PKV_ERR_WORKSPACE: workspace null, misaligned
  * or too small.

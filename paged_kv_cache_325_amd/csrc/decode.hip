@@ -51,8 +51,12 @@ namespace pkv {
 
 namespace {
 
-// Workgroups the automatic split plan aims for.  Large batches: 8192 over
-// the 256 CUs, enough for balance.  Small batches: 1024, so each workgroup
+// Workgroups the automatic split plan aims for.  The plan is a function of
+// the arguments only -- not of the device -- so that
+// pkv_paged_decode_workspace_bytes can size the workspace on the host
+// without a device query and results do not change between parts; the
+// targets are tuned for the 256 CUs of MI355X.  Large batches: 8192, 32 per
+// CU, enough for balance.  Small batches: 1024, so each workgroup
 // streams several chunks and its loads overlap its compute -- used while
 // that leaves at most kSmallPlanChunks 64-token chunks per workgroup.
 // Measured on the 28-layer fused decode step (graph-replayed, 16 / 8

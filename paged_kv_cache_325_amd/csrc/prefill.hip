@@ -556,10 +556,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
   int queue = blockIdx.x % nq;
   int exhausted = 0;  // queues found empty so far
   // blocking pull: the next item, or -1 once every queue is exhausted
+  // A workspace that was not zero before the first call holds arbitrary
+  // counters: an id outside [0, num_items) then counts as an exhausted queue,
+  // so such a call computes wrong rows but never indexes past the problem.
   auto pull = [&]() -> int {
     while (exhausted < nq) {
-      const int id = queue + atomicAdd(&a.counters[queue], 1) * nq;
-      if (id < a.num_items) return id;
+      const int ticket = atomicAdd(&a.counters[queue], 1);
+      const int64_t id = queue + (int64_t)ticket * nq;
+      if (ticket >= 0 && id < a.num_items) return (int)id;
       queue = queue + 1 == nq ? 0 : queue + 1;
       ++exhausted;
     }

@@ -407,6 +407,36 @@ def test_prefill_workspace_reset_and_small_grids(spec):
     assert_close(outs[0].double().cpu().numpy(), expected(w), spec.name)
 
 
+def test_prefill_workspace_not_zeroed_is_contained():
+    """A workspace whose queue counters were never zeroed (here every counter
+    holds -2^30) breaks the work queues, not memory: every ticket is outside
+    the item range, so each queue counts as exhausted, the kernel ends and no
+    output row is touched.  A zeroed workspace then gives the oracle's
+    result."""
+    w = build([s for s in SMALL if s.name == "pre-bf16-g4"][0])
+    d = to_device(w)
+    check_inputs(d)
+    store(d)
+    n = pkv.pkv_paged_prefill_workspace_bytes() // 4
+    bad = torch.full((n,), -(1 << 30), dtype=torch.int32, device="cuda")
+    out = torch.full((w.num_tokens, w.num_q_heads, 128), float("nan"), dtype=torch.bfloat16,
+                     device="cuda")
+    announce("prefill with a workspace that was not zeroed")
+    pkv.pkv_paged_prefill_varlen(d.q, d.k_cache, d.v_cache, d.cu_seqlens_q, w.max_seqlen_q,
+                                 d.context_lens, w.max_context_len, d.block_tables, w.scale,
+                                 out=out, workspace=bad)
+    torch.cuda.synchronize()
+    assert torch.isnan(out.float()).all()
+    announce("prefill with a zeroed workspace after it")
+    good = torch.zeros(n, dtype=torch.int32, device="cuda")
+    pkv.pkv_paged_prefill_varlen(d.q, d.k_cache, d.v_cache, d.cu_seqlens_q, w.max_seqlen_q,
+                                 d.context_lens, w.max_context_len, d.block_tables, w.scale,
+                                 out=out, workspace=good)
+    torch.cuda.synchronize()
+    assert int(good.abs().sum()) == 0
+    assert_close(out.double().cpu().numpy(), expected(w), "after a bad workspace")
+
+
 # ---------------------------------------------------------------------------
 # the five full-size workloads
 # ---------------------------------------------------------------------------

@@ -55,3 +55,56 @@ def test_noalloc_step_fp32_after_bf16():
     # fp32 partials of another shape over the same scratch
     w = build(Spec("noalloc-fp32", "decode", "fp32", 8, 2, [700, 1500, 3], [1] * 3, 9502))
     _step_both_ways(w, 3)
+
+
+def test_noalloc_step_replayed_from_a_graph():
+    """The callers this entry point is for capture it: one step captured in a
+    HIP graph (torch's capture) and replayed three times on fresh inputs
+    copied into the captured buffers, with eager work in between, each
+    replay bitwise equal to the step with a caller workspace run eagerly."""
+    w = build(Spec("noalloc-graph", "decode", "bf16", 16, 8, [3000, 17, 900, 1, 2049, 4096],
+                   [1] * 6, 9503))
+    hq, hkv = w.num_q_heads, w.num_kv_heads
+    assert pkv.pkv_paged_decode_workspace_bytes(w.batch, hq, hkv, 128, w.max_context_len,
+                                                w.block_size, 0) > 0
+    g_in = to_device(w)
+    check_inputs(g_in)
+    k0, v0 = g_in.k_cache.clone(), g_in.v_cache.clone()
+    out = torch.empty((w.batch, hq, 128), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        pkv.pkv_paged_decode_step_noalloc(g_in.q, g_in.k, g_in.v, g_in.slot_mapping,
+                                          g_in.k_cache, g_in.v_cache, g_in.block_tables,
+                                          g_in.context_lens, w.max_context_len, w.scale, out=out)
+
+    announce("no-alloc step: warm-up on a side stream, then capture")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    gen = torch.Generator().manual_seed(9504)
+    for rep in range(3):
+        fresh = torch.randn(g_in.qkv.shape, generator=gen).to(torch.bfloat16).cuda()
+        g_in.qkv.copy_(fresh)
+        g_in.k_cache.copy_(k0)
+        g_in.v_cache.copy_(v0)
+        announce(f"no-alloc step: replay {rep}")
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        kc_got, vc_got = g_in.k_cache.clone(), g_in.v_cache.clone()
+        ref = to_device(w)
+        ref.qkv.copy_(fresh)
+        want = pkv.pkv_paged_decode_step(ref.q, ref.k, ref.v, ref.slot_mapping, ref.k_cache,
+                                         ref.v_cache, ref.block_tables, ref.context_lens,
+                                         w.max_context_len, w.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"replay {rep}"
+        assert torch.equal(kc_got.view(torch.int16), ref.k_cache.view(torch.int16))
+        assert torch.equal(vc_got.view(torch.int16), ref.v_cache.view(torch.int16))
