@@ -11,6 +11,9 @@ imports it, and this package never imports the product path.
 ``brute`` pure-Python loop versions of decode, prefill and contiguous
           prefill for tiny inputs, written independently of ``ref`` to pin
           it.
+``prefix_plan`` the shared-prefix decode plan (which sequences' leading
+          splits are computed once for a group), in plain Python.
+``block_manager`` the host block manager's allocation algorithms.
 
 Parity status: every function here is pinned by CPU tests (brute force,
 library SDPA on contiguous tensors, closed forms, invariants and the worked
