@@ -36,7 +36,7 @@ out here step by step:
    for each member (those splits are computed by the subgroup).
 
 Plan words (int32), in this order:
-  S, number of items, batch, number of subgroups P;
+  S, number of items, batch, G, number of subgroups P;
   skip[0 .. batch - 1];
   per subgroup: member count, then 16 member ids (unused: -1);
   per item: subgroup index, split index.
@@ -47,7 +47,7 @@ from __future__ import annotations
 from typing import List, Sequence
 
 MEMBER_SLOTS = 16  # query columns of one subgroup's tile
-HEADER_WORDS = 4
+HEADER_WORDS = 5
 
 
 def plan_words_bound(batch: int, max_context_len: int, split_tokens: int) -> int:
@@ -127,7 +127,7 @@ def prefix_plan(block_tables: Sequence[Sequence[int]], context_lens: Sequence[in
                 for b in run:
                     skip[b] = k
                 items.extend([p, s] for s in range(k))
-    words = [S, len(items), batch, len(subgroups)]
+    words = [S, len(items), batch, group, len(subgroups)]
     words += skip
     for run in subgroups:
         words += [len(run)] + run + [-1] * (MEMBER_SLOTS - len(run))
@@ -138,7 +138,7 @@ def prefix_plan(block_tables: Sequence[Sequence[int]], context_lens: Sequence[in
 
 def decode_plan(words: Sequence[int]):
     """The plan's parts: (S, batch, skip, subgroups, items)."""
-    S, n_items, batch, n_sub = words[:HEADER_WORDS]
+    S, n_items, batch, _group, n_sub = words[:HEADER_WORDS]
     o = HEADER_WORDS
     skip = list(words[o:o + batch])
     o += batch

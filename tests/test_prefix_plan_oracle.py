@@ -163,7 +163,7 @@ def test_groups_above_eight_share_nothing():
     tables, ctx = random_batch(7, 16, 64)
     for G in (16, 32):
         words = pp.prefix_plan(tables, ctx, 16, G, 64)
-        assert words[1] == 0 and words[3] == 0 and words[4:] == [0] * len(ctx)
+        assert words[1] == 0 and words[4] == 0 and words[5:] == [0] * len(ctx)
 
 
 # ---------------------------------------------------------------------------
