@@ -276,6 +276,96 @@ pkv_status pkv_paged_decode_step_noalloc(
     int32_t block_size, int64_t num_blocks, float scale, int32_t num_splits,
     void* out, void* stream);
 
+/*
+ * Shared-prefix decode.  Sequences whose block tables begin with the same
+ * physical blocks hold the same K/V there (architecture page, "Hash-basiertes
+ * Prefix Caching" and "Kern-Designentscheidungen" item 2: full prompt blocks
+ * with a cached chained hash are given the cached block, so sequences with a
+ * common prompt prefix share them).  The decode can then attend each shared
+ * split once for all of them: one MFMA tile per (shared split, kv head) whose
+ * columns are the members' query heads, merged per sequence with its private
+ * splits by the usual split-K merge.  The grouping is this library's own rule
+ * (the pages describe none), built on the host from the host copies of the
+ * tables by pkv_decode_prefix_plan:
+ *   - only whole decode splits (S keys: pkv_paged_decode_split_tokens) that
+ *     lie before every member's last position (ctx - 1) are shared;
+ *   - sequences are classed by first block id, ordered by their table rows
+ *     (lexicographically, over the blocks holding keys 0 .. ctx - 2), cut into
+ *     runs of 16 / G members (G = num_q_heads / num_kv_heads; G > 8 shares
+ *     nothing), and a run shares k = min(common entries * B, min ctx - 1) / S
+ *     splits.
+ *
+ * pkv_decode_prefix_plan_words -- int32 words that always suffice for the
+ * plan of `batch` sequences of at most max_context_len keys at split length
+ * split_tokens; -1 for negative sizes or split_tokens <= 0.
+ *
+ * pkv_decode_prefix_plan -- builds the plan (host code, no HIP call).
+ *   block_tables   HOST int32 [batch][max_blocks_per_seq] (the decode's
+ *                  tables, a host copy)
+ *   context_lens   HOST int32 [batch]; each <= max_blocks_per_seq * block_size
+ *   split_tokens   S of the decode call the plan is for, a positive multiple of
+ *                  64 (pkv_paged_decode_split_tokens with the same arguments)
+ *   plan           HOST int32 [plan_words], written: the plan (layout: S,
+ *                  items, batch, G, subgroups P; skip[batch]; P records of a
+ *                  member count and 16 member ids (-1 unused); items x
+ *                  (subgroup, split)); copy it to the device for the decode
+ *   num_items      HOST out: items (shared splits; 0 = nothing is shared)
+ *   words_written  HOST out (may be NULL): words of the plan
+ * Errors: PKV_ERR_INVALID (bad sizes, null pointers, a context longer than its
+ * table row), PKV_ERR_UNSUPPORTED (block size), PKV_ERR_WORKSPACE (plan_words
+ * too small).
+ *
+ * pkv_paged_decode_prefix -- pkv_paged_decode with a plan: the same
+ * arguments plus
+ *   prefix_plan    device int32 words of pkv_decode_prefix_plan, built from
+ *                  the same tables and context lengths (4-byte aligned)
+ *   prefix_items   the num_items the planner returned; 0 = pkv_paged_decode
+ *                  (bitwise)
+ * and the same workspace size.  bf16 only when prefix_items > 0
+ * (PKV_ERR_UNSUPPORTED otherwise).  Outputs match the oracle within the same
+ * tolerance as pkv_paged_decode; they are not bitwise equal to it (the shared
+ * splits run on MFMA with bf16 probabilities).  A plan whose header (S,
+ * items, batch, G) does not match the call is ignored: the result is then
+ * pkv_paged_decode's.  A plan built from other tables or context lengths
+ * gives NaN output rows for the sequences whose shared split does not hold
+ * in the tables passed (the kernel checks every member's table entries and
+ * context length); other malformed plan contents are undefined behaviour.
+ *
+ * pkv_paged_decode_step_prefix -- pkv_paged_decode_step with a plan (same
+ * extra arguments): the fused store plus the shared-prefix decode.  The
+ * stored row (position ctx - 1) lies past every shared split.
+ */
+int64_t pkv_decode_prefix_plan_words(int32_t batch, int32_t max_context_len,
+                                     int32_t split_tokens);
+
+pkv_status pkv_decode_prefix_plan(const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t batch,
+                                  int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t block_size, int32_t split_tokens,
+                                  int32_t* plan, int64_t plan_words,
+                                  int32_t* num_items, int64_t* words_written);
+
+pkv_status pkv_paged_decode_prefix(
+    pkv_dtype dtype, const void* q, int64_t q_token_stride, const void* k_cache,
+    const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, int32_t max_context_len, int32_t batch,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int64_t num_blocks, float scale, int32_t num_splits,
+    const int32_t* prefix_plan, int32_t prefix_items, void* out,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+pkv_status pkv_paged_decode_step_prefix(
+    pkv_dtype dtype, const void* q, int64_t q_token_stride, const void* k_new,
+    int64_t k_new_token_stride, const void* v_new, int64_t v_new_token_stride,
+    const int32_t* slot_mapping, void* k_cache, void* v_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, int32_t max_context_len, int32_t batch,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int64_t num_blocks, float scale, int32_t num_splits,
+    const int32_t* prefix_plan, int32_t prefix_items, void* out,
+    void* workspace, size_t workspace_bytes, void* stream);
+
 pkv_status pkv_paged_decode_merge(pkv_dtype dtype, const int32_t* context_lens,
                                   int32_t max_context_len, int32_t batch,
                                   int32_t num_q_heads, int32_t num_kv_heads,

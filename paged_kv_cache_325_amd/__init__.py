@@ -9,7 +9,10 @@ missing or a tensor is not on the GPU, the call raises.
 Names follow the C ABI: ``pkv_kv_store``, ``pkv_paged_decode`` (and its two
 halves ``pkv_paged_decode_partials`` / ``pkv_paged_decode_merge``),
 ``pkv_paged_decode_step`` (store fused into decode), ``pkv_paged_decode_step_noalloc``
-(the same without a workspace), ``pkv_paged_decode_workspace_bytes``,
+(the same without a workspace), ``pkv_decode_prefix_plan`` /
+``pkv_decode_prefix_plan_words`` (host planner of the shared-prefix decode),
+``pkv_paged_decode_prefix`` and ``pkv_paged_decode_step_prefix`` (decode with
+that plan), ``pkv_paged_decode_workspace_bytes``,
 ``pkv_paged_decode_split_tokens``, ``pkv_paged_prefill_workspace_bytes``,
 ``pkv_paged_prefill_varlen``, ``pkv_prefill_varlen`` (contiguous k/v, no cache),
 ``pkv_kv_block_bytes``, ``pkv_last_error``.
@@ -28,6 +31,8 @@ __all__ = [
     "PKV_FP32", "PKV_BF16", "PkvError", "lib_path", "load_library",
     "pkv_kv_store", "pkv_paged_decode", "pkv_paged_decode_partials", "pkv_paged_decode_merge",
     "pkv_paged_decode_step", "pkv_paged_decode_step_noalloc", "PKV_NOALLOC_SCRATCH_BYTES",
+    "pkv_decode_prefix_plan_words", "pkv_decode_prefix_plan", "pkv_paged_decode_prefix",
+    "pkv_paged_decode_step_prefix",
     "pkv_paged_decode_workspace_bytes",
     "pkv_paged_decode_split_tokens", "pkv_paged_prefill_varlen",
     "pkv_paged_prefill_workspace_bytes", "pkv_prefill_varlen", "pkv_kv_block_bytes",
@@ -83,6 +88,20 @@ def load_library() -> ctypes.CDLL:
                                                   c_p, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32,
                                                   c_i32, c_i32, c_i32, c_i64, c_f, c_i32, c_p,
                                                   c_p]
+    lib.pkv_decode_prefix_plan_words.restype = c_i64
+    lib.pkv_decode_prefix_plan_words.argtypes = [c_i32, c_i32, c_i32]
+    lib.pkv_decode_prefix_plan.restype = c_i32
+    lib.pkv_decode_prefix_plan.argtypes = [c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_p,
+                                           c_i64, c_p, c_p]
+    lib.pkv_paged_decode_prefix.restype = c_i32
+    lib.pkv_paged_decode_prefix.argtypes = [c_i32, c_p, c_i64, c_p, c_p, c_p, c_i32, c_p, c_i32,
+                                            c_i32, c_i32, c_i32, c_i32, c_i32, c_i64, c_f, c_i32,
+                                            c_p, c_i32, c_p, c_p, ctypes.c_size_t, c_p]
+    lib.pkv_paged_decode_step_prefix.restype = c_i32
+    lib.pkv_paged_decode_step_prefix.argtypes = [c_i32, c_p, c_i64, c_p, c_i64, c_p, c_i64, c_p,
+                                                 c_p, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32,
+                                                 c_i32, c_i32, c_i32, c_i64, c_f, c_i32, c_p,
+                                                 c_i32, c_p, c_p, ctypes.c_size_t, c_p]
     lib.pkv_paged_decode_merge.restype = c_i32
     lib.pkv_paged_decode_merge.argtypes = [c_i32, c_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                            c_i32, c_p, c_p, ctypes.c_size_t, c_p]
@@ -199,7 +218,7 @@ def pkv_paged_decode_split_tokens(batch: int, num_q_heads: int, num_kv_heads: in
 
 
 def _decode_call(fn_name, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
-                 scale, out, workspace, num_splits, stream):
+                 scale, out, workspace, num_splits, stream, plan=None):
     lib = load_library()
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _gpu(t, n)
@@ -227,8 +246,64 @@ def _decode_call(fn_name, q, k_cache, v_cache, block_tables, context_lens, max_c
     _check(getattr(lib, fn_name)(
         _dtype_code(q), _ptr(q), qs, _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), max_blocks,
         _ptr(context_lens), int(max_context_len), batch, hq, hkv, d, bs, nblk, float(scale),
-        int(num_splits), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+        int(num_splits), *([] if plan is None else list(plan)), _ptr(out), _ptr(workspace),
+        ws_bytes, _stream(stream)))
     return out, workspace
+
+
+def _plan_args(prefix_plan: Optional[torch.Tensor], prefix_items: int):
+    """Pointer and item count of a device plan (None: no plan)."""
+    if prefix_plan is None:
+        if prefix_items:
+            raise ValueError("prefix_items > 0 needs a prefix_plan")
+        return (None, 0)
+    _int32(prefix_plan, "prefix_plan")
+    return (_ptr(prefix_plan), int(prefix_items))
+
+
+def pkv_decode_prefix_plan_words(batch: int, max_context_len: int, split_tokens: int) -> int:
+    return int(load_library().pkv_decode_prefix_plan_words(batch, max_context_len, split_tokens))
+
+
+def pkv_decode_prefix_plan(block_tables, context_lens, num_q_heads: int, num_kv_heads: int,
+                           block_size: int, split_tokens: int):
+    """Host planner of the shared-prefix decode (include/pkv.h): from the HOST
+    block tables [batch, max_blocks] and context lengths [batch] (int32, torch
+    CPU tensors or numpy arrays), returns (plan, items): the plan as an int32
+    CPU tensor (copy it to the GPU for the decode) and its number of items."""
+    lib = load_library()
+    bt = torch.as_tensor(block_tables).to(torch.int32).contiguous()
+    cl = torch.as_tensor(context_lens).to(torch.int32).contiguous()
+    if bt.is_cuda or cl.is_cuda:
+        raise ValueError("the planner reads host copies of the tables and context lengths")
+    if bt.dim() != 2 or cl.dim() != 1 or bt.shape[0] != cl.shape[0]:
+        raise ValueError("block_tables must be [batch, max_blocks] and context_lens [batch]")
+    batch, max_blocks = int(bt.shape[0]), int(bt.shape[1])
+    max_ctx = int(cl.max()) if batch else 0
+    cap = pkv_decode_prefix_plan_words(batch, max(max_ctx, 0), split_tokens)
+    if cap < 0:
+        raise ValueError("bad batch or split_tokens")
+    buf = torch.empty(cap, dtype=torch.int32)
+    items, words = ctypes.c_int32(0), ctypes.c_int64(0)
+    _check(lib.pkv_decode_prefix_plan(bt.data_ptr(), max_blocks, cl.data_ptr(), batch,
+                                      num_q_heads, num_kv_heads, block_size, split_tokens,
+                                      buf.data_ptr(), cap, ctypes.byref(items),
+                                      ctypes.byref(words)))
+    return buf[: words.value].clone(), int(items.value)
+
+
+def pkv_paged_decode_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            block_tables: torch.Tensor, context_lens: torch.Tensor,
+                            max_context_len: int, scale: float,
+                            prefix_plan: Optional[torch.Tensor], prefix_items: int,
+                            out: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None, num_splits: int = 0,
+                            stream=None) -> torch.Tensor:
+    """pkv_paged_decode with a shared-prefix plan (a device int32 tensor from
+    pkv_decode_prefix_plan for the same tables, lengths and split length)."""
+    return _decode_call("pkv_paged_decode_prefix", q, k_cache, v_cache, block_tables,
+                        context_lens, max_context_len, scale, out, workspace, num_splits, stream,
+                        plan=_plan_args(prefix_plan, prefix_items))[0]
 
 
 def pkv_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -299,6 +374,33 @@ def pkv_paged_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Ten
     _check(lib.pkv_paged_decode_step(
         *head, int(max_context_len), batch, hq, hkv, d, bs, nblk, float(scale),
         int(num_splits), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def pkv_paged_decode_step_prefix(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                                 slot_mapping: torch.Tensor, k_cache: torch.Tensor,
+                                 v_cache: torch.Tensor, block_tables: torch.Tensor,
+                                 context_lens: torch.Tensor, max_context_len: int, scale: float,
+                                 prefix_plan: Optional[torch.Tensor], prefix_items: int,
+                                 out: Optional[torch.Tensor] = None,
+                                 workspace: Optional[torch.Tensor] = None, num_splits: int = 0,
+                                 stream=None) -> torch.Tensor:
+    """pkv_paged_decode_step with a shared-prefix plan (see
+    pkv_paged_decode_prefix)."""
+    lib = load_library()
+    if out is None:
+        _gpu(q, "q")
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    batch, hq, hkv, d, bs, nblk, head = _step_args(q, k_new, v_new, slot_mapping, k_cache,
+                                                   v_cache, block_tables, context_lens, out)
+    need = pkv_paged_decode_workspace_bytes(batch, hq, hkv, d, max_context_len, bs, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.pkv_paged_decode_step_prefix(
+        *head, int(max_context_len), batch, hq, hkv, d, bs, nblk, float(scale),
+        int(num_splits), *_plan_args(prefix_plan, prefix_items), _ptr(out), _ptr(workspace),
+        ws_bytes, _stream(stream)))
     return out
 
 

@@ -43,7 +43,12 @@ def gxx() -> str:
 # prefill.hip: no NaN reaches its max reductions (masked scores are -inf via
 # an integer-compare select), so fmaxf needs no NaN canonicalisation; that
 # halves the VALU work of the row max.  Infinities keep their meaning.
-PER_FILE_FLAGS = {"prefill.hip": ["-fno-honor-nans"]}
+# decode.hip: the MFMA accumulators of the shared-prefix path stay in VGPRs
+# (the default puts them in AGPRs, which count against the same per-SIMD
+# register file and took the kernel from two waves per SIMD to one); the
+# kernels without MFMA compile to the same code either way.
+PER_FILE_FLAGS = {"prefill.hip": ["-fno-honor-nans"],
+                  "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _flags():

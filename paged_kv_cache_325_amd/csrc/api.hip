@@ -201,6 +201,12 @@ struct FusedStore {
   const int32_t* slot_mapping;
 };
 
+// A shared-prefix plan (device words from pkv_decode_prefix_plan).
+struct PrefixArg {
+  const int32_t* plan;
+  int32_t items;
+};
+
 // Checks for the merge (and shared by the split) entry points.
 pkv_status check_decode_common(pkv_dtype dtype, int32_t batch, int32_t num_q_heads,
                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
@@ -248,7 +254,8 @@ pkv_status decode_parts(int parts, pkv_dtype dtype, const void* q, int64_t q_tok
                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                         int64_t num_blocks, float scale, int32_t num_splits, void* out,
                         void* workspace, size_t workspace_bytes, void* stream,
-                        const FusedStore* fs = nullptr, bool use_scratch = false) {
+                        const FusedStore* fs = nullptr, bool use_scratch = false,
+                        const PrefixArg* pa = nullptr) {
   const int eb = elem_bytes(dtype);
   if (eb == 0) return fail(PKV_ERR_INVALID, "unknown dtype %d", (int)dtype);
   pkv_status st = check_geometry(num_q_heads, num_kv_heads, head_dim, block_size);
@@ -291,6 +298,20 @@ pkv_status decode_parts(int parts, pkv_dtype dtype, const void* q, int64_t q_tok
     if (num_blocks * block_size > (int64_t)INT32_MAX + 1)
       return fail(PKV_ERR_UNSUPPORTED, "num_blocks * block_size exceeds the int32 slot range");
   }
+  if (pa && pa->items != 0) {
+    if (pa->items < 0) return fail(PKV_ERR_INVALID, "prefix_items (%d) < 0", pa->items);
+    if (dtype != PKV_BF16)
+      return fail(PKV_ERR_UNSUPPORTED, "shared-prefix decode supports bf16 only");
+    if (pkv::kPlanMembers / (num_q_heads / num_kv_heads) < 2)
+      return fail(PKV_ERR_INVALID, "no shared-prefix plan has items for GQA group size %d",
+                  num_q_heads / num_kv_heads);
+    if (!pa->plan || ((uintptr_t)pa->plan & 3) != 0)
+      return fail(PKV_ERR_INVALID, "prefix_plan must be a non-null, 4-byte aligned pointer");
+    const int64_t grid = (int64_t)plan.nsplit * batch * num_kv_heads * plan.head_chunks +
+                         (int64_t)pa->items * num_kv_heads;
+    if (grid > INT32_MAX)
+      return fail(PKV_ERR_UNSUPPORTED, "too many workgroups (%lld) for one launch", (long long)grid);
+  }
   pkv::DecodeLaunch l;
   l.q = q;
   l.q_stride = q_token_stride;
@@ -311,6 +332,10 @@ pkv_status decode_parts(int parts, pkv_dtype dtype, const void* q, int64_t q_tok
     void* ptr = nullptr;
     if ((st = scratch_for_current_device(&ptr)) != PKV_OK) return st;
     l.workspace = (float*)ptr;
+  }
+  if (pa && pa->items > 0 && (parts & kSplitOnly)) {
+    l.prefix_plan = pa->plan;
+    l.prefix_items = pa->items;
   }
   if (fs) {
     l.k_new = fs->k_new;
@@ -380,6 +405,84 @@ pkv_status pkv_paged_decode_step_noalloc(pkv_dtype dtype, const void* q, int64_t
                       max_blocks_per_seq, context_lens, max_context_len, batch, num_q_heads,
                       num_kv_heads, head_dim, block_size, num_blocks, scale, num_splits, out,
                       nullptr, 0, stream, &fs, /*use_scratch=*/true);
+}
+
+int64_t pkv_decode_prefix_plan_words(int32_t batch, int32_t max_context_len,
+                                     int32_t split_tokens) {
+  if (batch < 0 || max_context_len < 0 || split_tokens <= 0) return -1;
+  return pkv::prefix_plan_words_bound(batch, max_context_len, split_tokens);
+}
+
+pkv_status pkv_decode_prefix_plan(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t batch,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t block_size,
+                                  int32_t split_tokens, int32_t* plan, int64_t plan_words,
+                                  int32_t* num_items, int64_t* words_written) {
+  if (batch < 0 || max_blocks_per_seq < 0)
+    return fail(PKV_ERR_INVALID, "batch and max_blocks_per_seq must be >= 0");
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                num_q_heads, num_kv_heads);
+  if (!pkv::block_size_supported(block_size))
+    return fail(PKV_ERR_UNSUPPORTED,
+                "block_size %d is not supported (16, 32, or a multiple of 64 up to %d)",
+                block_size, pkv::kMaxBlockSize);
+  if (split_tokens <= 0 || split_tokens % 64 != 0)
+    return fail(PKV_ERR_INVALID, "split_tokens (%d) must be a positive multiple of 64",
+                split_tokens);
+  if (!plan || !num_items) return fail(PKV_ERR_INVALID, "null plan or num_items");
+  if (batch > 0 && (!block_tables || !context_lens))
+    return fail(PKV_ERR_INVALID, "null block_tables or context_lens with batch = %d", batch);
+  for (int b = 0; b < batch; ++b)
+    if ((int64_t)context_lens[b] > (int64_t)max_blocks_per_seq * block_size)
+      return fail(PKV_ERR_INVALID,
+                  "context_lens[%d] (%d) > max_blocks_per_seq (%d) * block_size", b,
+                  context_lens[b], max_blocks_per_seq);
+  int32_t items = 0;
+  const int64_t words = pkv::build_prefix_plan(block_tables, max_blocks_per_seq, context_lens,
+                                               batch, block_size, num_q_heads / num_kv_heads,
+                                               split_tokens, plan, plan_words, &items);
+  if (words < 0)
+    return fail(PKV_ERR_WORKSPACE,
+                "plan buffer of %lld words is too small (pkv_decode_prefix_plan_words gives a "
+                "size that always suffices)",
+                (long long)plan_words);
+  *num_items = items;
+  if (words_written) *words_written = words;
+  return PKV_OK;
+}
+
+pkv_status pkv_paged_decode_prefix(pkv_dtype dtype, const void* q, int64_t q_token_stride,
+                                   const void* k_cache, const void* v_cache,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens, int32_t max_context_len,
+                                   int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                   float scale, int32_t num_splits, const int32_t* prefix_plan,
+                                   int32_t prefix_items, void* out, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  const PrefixArg pa{prefix_plan, prefix_items};
+  return decode_parts(kSplitAndMerge, dtype, q, q_token_stride, k_cache, v_cache, block_tables,
+                      max_blocks_per_seq, context_lens, max_context_len, batch, num_q_heads,
+                      num_kv_heads, head_dim, block_size, num_blocks, scale, num_splits, out,
+                      workspace, workspace_bytes, stream, nullptr, false, &pa);
+}
+
+pkv_status pkv_paged_decode_step_prefix(
+    pkv_dtype dtype, const void* q, int64_t q_token_stride, const void* k_new,
+    int64_t k_new_token_stride, const void* v_new, int64_t v_new_token_stride,
+    const int32_t* slot_mapping, void* k_cache, void* v_cache, const int32_t* block_tables,
+    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
+    int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int64_t num_blocks, float scale, int32_t num_splits,
+    const int32_t* prefix_plan, int32_t prefix_items, void* out, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  const FusedStore fs{k_new, k_new_token_stride, v_new, v_new_token_stride, slot_mapping};
+  const PrefixArg pa{prefix_plan, prefix_items};
+  return decode_parts(kSplitAndMerge, dtype, q, q_token_stride, k_cache, v_cache, block_tables,
+                      max_blocks_per_seq, context_lens, max_context_len, batch, num_q_heads,
+                      num_kv_heads, head_dim, block_size, num_blocks, scale, num_splits, out,
+                      workspace, workspace_bytes, stream, &fs, false, &pa);
 }
 
 pkv_status pkv_paged_decode_partials(pkv_dtype dtype, const void* q, int64_t q_token_stride,

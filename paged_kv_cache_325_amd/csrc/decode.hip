@@ -63,6 +63,21 @@ namespace {
 // query / kv heads, contexts of 512-4096): 1024 workgroups beat 8192 by
 // 8-15 % at batches 4-16 and ~3 % at 32; 8192 stays best at 64.
 constexpr int kTargetWaves = 256 * 32;
+// Compacted units (unit_of) cost each split workgroup ~1 us of latency
+// before its first load; they pay where the grid holds many empty units
+// (max_context_len spans at least kMinCompactSplits splits, so sequences
+// shorter than it leave most of theirs empty) and each unit carries
+// enough keys to hide that latency (kMinCompactSplit).  Measured with
+// interleaved A/B runs (bitwise-equal outputs): the 16-sequence
+// lognormal-length workload (64 splits of 512 keys) 125.7 -> 117.3 us; the
+// 64- and 256-sequence workloads (16 splits of 256 keys, 4 of 2048) within
+// 0.5 %; 28-layer graph-replayed steps at batch 16 (8 splits of 512 keys)
+// 4 % slower, at batch 2-8 (64-256-key splits) unchanged -- hence the
+// bounds.  The row walk costs a ballot per row and 64 sequences.
+constexpr int kMaxCompactBatch = 256;
+constexpr int kMinCompactSplits = 16;
+constexpr int kMaxCompactSplits = 1024;
+constexpr int kMinCompactSplit = 512;
 constexpr int kSmallTargetWaves = 1024;
 constexpr int kSmallPlanChunks = 16;
 
@@ -100,6 +115,16 @@ struct DecodeArgs {
   const int32_t* slot_mapping;
   uint8_t* k_cache_w;
   uint8_t* v_cache_w;
+  // Shared-prefix plan (device words, layout in pkv_internal.h): the first
+  // prefix_wgs = prefix_items * num_kv_heads workgroups attend the shared
+  // splits; split workgroups skip the splits their sequence's subgroup
+  // covers.  Used only by the kPrefix instantiations.
+  const int32_t* prefix_plan;
+  int32_t prefix_items, prefix_wgs;
+  // Compacted units (see unit_of): split workgroups enumerate only the
+  // (sequence, split) units that have work, in split-major order.
+  int32_t compact;
+  FastDiv sdiv;  // division by split_tokens
 };
 
 struct TrueTag { static constexpr bool value = true; };
@@ -119,11 +144,318 @@ __device__ __forceinline__ void unpack(const u32x4& w, float* f) {
   }
 }
 
+// ---- shared splits of a subgroup (bf16, MFMA) ------------------------------
+// A split that the sequences of a subgroup hold in the same physical blocks
+// (equal leading block-table entries: hash-based prefix caching gives
+// sequences with a common prompt prefix the same blocks) is attended once for
+// all of them.  The members' query heads of kv head g are the columns of one
+// v_mfma_f32_16x16x32_bf16 tile (at most 16: 16 / G members), the split's
+// keys its rows.  Per 32-key chunk: the K and V rows arrive in registers
+// (coalesced 1 KiB nontemporal loads, two chunks in flight), are staged in
+// LDS, and
+//   S^T (32 keys x 16 columns) = K Q^T      A: K rows from LDS, B: q
+//   online softmax per column, base 2
+//   O^T (128 dims x 16 columns) += V^T P^T  A: V^T by LDS transpose reads,
+//                                           B: P^T straight from S^T
+// MFMA layouts (16x16x32): lane l holds A[l%16][8(l/16)..+7],
+// B[8(l/16)..+7][l%16] and D[4(l/16)..+3][l%16].  The keys of a chunk are
+// ordered for the PV contraction as k = 8j + i -> key 4j + i (i < 4) and
+// 16 + 4j + i - 4 (i >= 4), which is where S^T left them in lane 16j + n.
+// Each member's (acc, m, l) is written to its own workspace slot of that
+// split, so the merge treats it as any other split.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;
+
+// A staged chunk: 32 key rows x 16 chunks of 16 bytes, for K and for V, with
+// chunk c of row r at position
+//   K: c ^ (r & 15)  -- the 16 rows of one A-operand read hit 16 distinct
+//                       16-byte bank groups;
+//   V: c ^ 2(r & 7)  -- the 8 rows of one half-wave transpose read hit 8
+//                       distinct 32-byte bank groups.
+__device__ __forceinline__ int pk_pos(int r, int c) { return c ^ (r & 15); }
+__device__ __forceinline__ int pv_pos(int r, int c) { return c ^ ((r & 7) << 1); }
+
+// kSmall: blocks of 16 or 32 tokens (each 1 KiB load of 4 rows gets its own
+// lookup); otherwise a 32-key chunk lies in one block.
+template <bool kSmall>
+__device__ __forceinline__ void prefix_split(const DecodeArgs& a, int id, u32x4* lds) {
+  const int lane = threadIdx.x;
+  const int g = id % a.num_kv_heads;
+  const int item = id / a.num_kv_heads;
+  const int32_t* plan = a.prefix_plan;
+  // a plan built for another split length, batch or GQA group is ignored
+  // (the split workgroups make the same test and then skip nothing)
+  if (plan[0] != a.split_tokens || plan[1] != a.prefix_items || plan[2] != a.batch ||
+      plan[3] != a.group)
+    return;
+  const int nsub = plan[4];
+  const int32_t* groups = plan + kPlanHeader + a.batch;
+  const int32_t* it = groups + (int64_t)kPlanGroupWords * nsub + 2 * item;
+  const int sg = it[0], s = it[1];
+  if (sg < 0 || sg >= nsub || s < 0 || s >= a.nsplit) return;
+  const int32_t* rec = groups + (int64_t)kPlanGroupWords * sg;
+  const int cnt = rec[0];
+  const int G = a.group;
+  if (cnt < 1 || cnt * G > kPlanMembers) return;
+
+  const int n = lane & 15;  // column: member n / G, query head g*G + n % G
+  const int j = lane >> 4;
+  const bool col_ok = n < cnt * G;
+  const int mi = col_ok ? n / G : 0;
+  const int b_col = rec[1 + mi];
+  const int h_col = g * G + (col_ok ? n - mi * G : 0);
+  const int S = a.split_tokens;
+  const int k_lo = s * S, k_hi = k_lo + S;
+
+  // The plan must match the tables: every member holds the split before its
+  // last position, in the same blocks.  A plan that does not (built for
+  // other tables) gives NaN for the members' outputs instead of wrong rows.
+  bool bad;
+  {
+    const int bi = lane < cnt ? rec[1 + lane] : 0;
+    const bool id_ok = bi >= 0 && bi < a.batch;
+    const int ni = (lane < cnt && id_ok) ? a.context_lens[bi] : 0x7fffffff;
+    bad = __builtin_amdgcn_ballot_w64(lane < cnt && (!id_ok || ni <= k_hi)) != 0;
+  }
+  const uint32_t bs = a.bdiv.d;
+  const int blk_lo = (int)a.bdiv.div((uint32_t)k_lo);
+  const int nblk = (int)a.bdiv.div((uint32_t)(k_hi - 1)) - blk_lo + 1;
+  bad |= nblk > 64;
+  int tab = 0;
+  if (!bad) {
+    tab = lane < nblk ? a.block_tables[(int64_t)rec[1] * a.max_blocks + blk_lo + lane] : 0;
+    for (int i = 1; i < cnt; ++i) {
+      const int ti = lane < nblk ? a.block_tables[(int64_t)rec[1 + i] * a.max_blocks + blk_lo + lane] : 0;
+      bad |= __builtin_amdgcn_ballot_w64(ti != tab) != 0;
+    }
+  }
+  if (bad) {
+    if (col_ok && j == 0 && b_col >= 0 && b_col < a.batch) {
+      const int64_t slot = ((int64_t)b_col * a.num_q_heads + h_col) * a.nsplit + s;
+      *reinterpret_cast<f32x2*>(a.ws_ml + slot * 2) = f32x2{NAN, NAN};
+    }
+    return;
+  }
+
+  // q^T columns: dims 32 ks + 8 j .. + 7 of the lane's column
+  u32x4 qf[4];
+  {
+    const uint8_t* qp = a.q + (int64_t)b_col * a.q_stride_bytes + (int64_t)h_col * 256 + j * 16;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qf[ks] = col_ok ? *reinterpret_cast<const u32x4*>(qp + ks * 64) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // byte offset of key row kk (kv head g) in the cache
+  auto row_base = [&](int kk) -> int64_t {
+    const uint32_t q = a.bdiv.div((uint32_t)kk);
+    const int64_t blk = __builtin_amdgcn_readlane(tab, (int)q - blk_lo);
+    return ((blk * a.num_kv_heads + g) * bs + (kk - q * bs)) * 256;
+  };
+  auto load = [&](u32x4 (&kr)[8], u32x4 (&vr)[8], int t) {
+    const int c0 = k_lo + 32 * t;
+    if constexpr (kSmall) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kr[i] = stream_load(a.k_cache + row_base(c0 + 4 * i) + lane * 16);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) vr[i] = stream_load(a.v_cache + row_base(c0 + 4 * i) + lane * 16);
+    } else {
+      const int64_t base = row_base(c0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kr[i] = stream_load(a.k_cache + base + i * 1024 + lane * 16);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) vr[i] = stream_load(a.v_cache + base + i * 1024 + lane * 16);
+    }
+  };
+
+  f32x4 o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_lane = 0.f;
+  const float c = a.scale_log2;
+  u32x4* kl = lds;
+  u32x4* vl = lds + 32 * 16;
+  const int ta = lane & 3, tm = (lane >> 2) & 3;
+
+  // One wave: its LDS accesses complete in order, so the previous chunk's
+  // operand reads are done before the next chunk's rows land.  Lane l of
+  // load i holds chunk l % 16 of row 4 i + l / 16.
+  auto stage = [&](const u32x4 (&kr)[8], const u32x4 (&vr)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + j;
+      kl[r * 16 + pk_pos(r, n)] = kr[i];
+      vl[r * 16 + pv_pos(r, n)] = vr[i];
+    }
+  };
+  auto compute = [&]() {
+    f32x4 sc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      sc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int r = 16 * mt + n;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        sc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            as_bf16x8(kl[r * 16 + pk_pos(r, 4 * ks + j)]), as_bf16x8(qf[ks]), sc[mt], 0, 0, 0);
+    }
+    // online softmax of the lane's 8 keys; a column's 32 keys are spread
+    // over lanes n, n + 16, n + 32, n + 48
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = sc[e >> 2][e & 3] * c;
+    float cm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                     fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+    cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+    const float mn = fmaxf(m_run, cm);
+    const float alpha = fast_exp2(m_run - mn);
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = fast_exp2(x[e] - mn);
+    const u32x4 pf = u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
+                           pack_bf16(p[6], p[7])};
+    // the row sum of the bf16 probabilities the PV product consumes
+    float ps = dot2_bf16(pf[0], kOnesBf16x2, 0.f);
+    ps = dot2_bf16(pf[1], kOnesBf16x2, ps);
+    ps = dot2_bf16(pf[2], kOnesBf16x2, ps);
+    ps = dot2_bf16(pf[3], kOnesBf16x2, ps);
+    l_lane = fmaf(l_lane, alpha, ps);
+    m_run = mn;
+    // the V^T operand reads are not hoisted above the softmax (registers)
+    __builtin_amdgcn_sched_barrier(0);
+    // O^T += V^T P^T.  ds_read_b64_tr_b16: in each 16-lane group, lane
+    // 4a + e receives element e of the 8-byte chunks addressed by lanes a,
+    // a + 4, a + 8, a + 12.  Lane 16 j + 4 tm + ta addresses key 4 j + tm
+    // (then 16 + 4 j + tm) at dims 16 dt + 4 ta, so lane 16 j + d receives
+    // dim 16 dt + d of keys 4 j .. 4 j + 3 (then 16 + 4 j ..).
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      o[dt] *= alpha;
+      const int dim = 16 * dt + 4 * ta;
+      const int r0 = 4 * j + tm, r1 = 16 + 4 * j + tm;
+      const char* p0 = reinterpret_cast<const char*>(vl) + r0 * 256 + pv_pos(r0, dim >> 3) * 16 + (dim & 7) * 2;
+      const char* p1 = reinterpret_cast<const char*>(vl) + r1 * 256 + pv_pos(r1, dim >> 3) * 16 + (dim & 7) * 2;
+      const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0));
+      const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p1));
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}),
+                                                      as_bf16x8(pf), o[dt], 0, 0, 0);
+    }
+  };
+
+  // One chunk in registers: it is loaded while the previous one is computed
+  // from LDS.
+  u32x4 kr[8], vr[8];
+  const int nch = S / 32;
+  load(kr, vr, 0);
+  for (int t = 0; t + 1 < nch; ++t) {
+    stage(kr, vr);
+    load(kr, vr, t + 1);
+    compute();
+  }
+  stage(kr, vr);
+  compute();
+
+  float l_col = l_lane + __shfl_xor(l_lane, 16, 64);
+  l_col += __shfl_xor(l_col, 32, 64);
+  if (col_ok) {
+    const int64_t slot = ((int64_t)b_col * a.num_q_heads + h_col) * a.nsplit + s;
+    float* dst = a.ws_acc + slot * kHeadDim + 4 * j;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(dst + 16 * dt) = o[dt];
+    if (j == 0) *reinterpret_cast<f32x2*>(a.ws_ml + slot * 2) = f32x2{m_run, l_col};
+  }
+}
+
 // kSmall: blocks shorter than a chunk (16 or 32 tokens, a power of two): each
 // 1 KiB load of a chunk still lies in one block, but consecutive loads of a
 // chunk may lie in different blocks, so each load gets its own block lookup.
 // Otherwise a chunk lies in one block and one lookup serves all its loads.
-template <int kElemBytes, int kHeads, bool kFused, bool kSmall>
+// Compacted units.  The host knows only max_context_len, so the grid has
+// nsplit units per sequence, and for skewed lengths most of them are empty:
+// those workgroups, interleaved in the dispatch order, delayed the
+// workgroups of the long sequences' last splits and so stretched the tail.
+// Here unit u of the launch is the u-th (sequence, split) that has work
+// (split s of sequence b for lo_b <= s < hi_b, hi_b = max(1, ceil(n_b / S)):
+// one unit for an empty context, which writes its zero row; lo_b = the
+// splits a shared-prefix subgroup computes), in split-major order (so the
+// same split of different sequences runs together, as before); units past
+// the last one exit at the end of the dispatch.  Every lane holds the
+// counts of sequences lane + 64 k (batch <= 256, the host's condition);
+// each row s costs a ballot per k.  Returns false for a unit past the end.
+template <bool kPrefix>
+__device__ __forceinline__ bool unit_of(const DecodeArgs& a, int u, int& b_out, int& s_out,
+                                        int& n_out) {
+  constexpr int kMaxK = kMaxCompactBatch / 64;
+  const int lane = threadIdx.x;
+  const int K = (a.batch + 63) >> 6;  // uniform, 1 .. kMaxK
+  bool plan_ok = false;
+  if constexpr (kPrefix) {
+    const int32_t* plan = a.prefix_plan;
+    plan_ok = plan[0] == a.split_tokens && plan[1] == a.prefix_items && plan[2] == a.batch &&
+              plan[3] == a.group;
+  }
+  int nb[kMaxK], lo[kMaxK], hi[kMaxK];
+  int mine = 0;
+#pragma unroll
+  for (int k = 0; k < kMaxK; ++k) {
+    nb[k] = lo[k] = hi[k] = 0;
+    if (k < K) {
+      const int bb = lane + 64 * k;
+      const bool in = bb < a.batch;
+      nb[k] = in ? a.context_lens[bb] : 0;
+      hi[k] = in ? max(1, (int)a.sdiv.div((uint32_t)nb[k] + a.split_tokens - 1)) : 0;
+      if constexpr (kPrefix)
+        lo[k] = (in && plan_ok) ? min(a.prefix_plan[kPlanHeader + bb], hi[k]) : 0;
+      mine += hi[k] - lo[k];
+    }
+  }
+  // units in all (exact in fp32: the host keeps batch * nsplit below 2^24);
+  // the units past the last one exit here
+  if ((float)u >= wave_sum((float)mine)) return false;
+  // walk the rows (splits) to the one holding unit u
+  int before = 0;
+  for (int s = 0; s < a.nsplit; ++s) {
+    uint64_t m[kMaxK];
+    int row = 0;
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) {
+      m[k] = 0;
+      if (k < K) {
+        m[k] = __builtin_amdgcn_ballot_w64(s >= lo[k] && s < hi[k]);
+        row += __builtin_popcountll(m[k]);
+      }
+    }
+    if (u < before + row) {
+      int r = u - before;
+#pragma unroll
+      for (int k = 0; k < kMaxK; ++k) {
+        const int c = __builtin_popcountll(m[k]);
+        if (r >= 0 && r < c) {
+          // the lane of the r-th set bit of m[k]
+          const int rank = __builtin_amdgcn_mbcnt_hi(
+              (uint32_t)(m[k] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m[k], 0));
+          const uint64_t hit = __builtin_amdgcn_ballot_w64(((m[k] >> lane) & 1) && rank == r);
+          const int l = __builtin_ffsll((long long)hit) - 1;
+          b_out = 64 * k + l;
+          n_out = __builtin_amdgcn_readlane(nb[k], l);
+        }
+        r -= c;
+      }
+      s_out = s;
+      return true;
+    }
+    before += row;
+  }
+  return false;
+}
+
+// kPrefix (bf16 only): the launch starts with the workgroups of a
+// shared-prefix plan's items, and split workgroups skip the splits a
+// subgroup covers.
+template <int kElemBytes, int kHeads, bool kFused, bool kSmall, bool kPrefix>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   using S = DecodeShape<kElemBytes>;
   constexpr int kVec = S::kVec;
@@ -137,14 +469,26 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 
   const int lane = threadIdx.x;
   int id = blockIdx.x;
+  if constexpr (kPrefix) {
+    static_assert(kElemBytes == 2, "shared splits are bf16 only");
+    if (id < a.prefix_wgs) {
+      prefix_split<kSmall>(a, id, k_lds);
+      return;
+    }
+    id -= a.prefix_wgs;
+  }
   const int hc = id % a.head_chunks;
   id /= a.head_chunks;
   const int g = id % a.num_kv_heads;
   id /= a.num_kv_heads;
-  const int b = id % a.batch;
-  const int s = id / a.batch;
-
-  const int n = a.context_lens[b];
+  int b, s, n;
+  if (a.compact) {
+    if (!unit_of<kPrefix>(a, id, b, s, n)) return;
+  } else {
+    b = id % a.batch;
+    s = id / a.batch;
+    n = a.context_lens[b];
+  }
   const int start = s * a.split_tokens;
   const int h0 = g * a.group + hc * kHeads;
 
@@ -174,6 +518,14 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         *reinterpret_cast<u32x4*>(a.v_cache_w + off) = vnew;
       }
     }
+  }
+  if constexpr (kPrefix) {
+    // splits computed once for the sequence's subgroup (after the fused
+    // store above: the stored row lies past every shared split)
+    const int32_t* plan = a.prefix_plan;
+    if (plan[0] == a.split_tokens && plan[1] == a.prefix_items && plan[2] == a.batch &&
+        plan[3] == a.group && s < plan[kPlanHeader + b])
+      return;
   }
   if (start >= n) {
     if (s == 0) {  // empty context: zero output rows
@@ -507,11 +859,22 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 
 template <int kElemBytes, int kHeads, bool kSmall>
 void launch_split_b(const DecodeArgs& args, unsigned grid, hipStream_t stream) {
+  if constexpr (kElemBytes == 2) {
+    if (args.prefix_plan) {
+      if (args.k_new)
+        hipLaunchKernelGGL((decode_split_kernel<2, kHeads, true, kSmall, true>), dim3(grid),
+                           dim3(64), 0, stream, args);
+      else
+        hipLaunchKernelGGL((decode_split_kernel<2, kHeads, false, kSmall, true>), dim3(grid),
+                           dim3(64), 0, stream, args);
+      return;
+    }
+  }
   if (args.k_new)
-    hipLaunchKernelGGL((decode_split_kernel<kElemBytes, kHeads, true, kSmall>), dim3(grid),
+    hipLaunchKernelGGL((decode_split_kernel<kElemBytes, kHeads, true, kSmall, false>), dim3(grid),
                        dim3(64), 0, stream, args);
   else
-    hipLaunchKernelGGL((decode_split_kernel<kElemBytes, kHeads, false, kSmall>), dim3(grid),
+    hipLaunchKernelGGL((decode_split_kernel<kElemBytes, kHeads, false, kSmall, false>), dim3(grid),
                        dim3(64), 0, stream, args);
 }
 
@@ -616,13 +979,22 @@ static DecodeArgs decode_args(int elem_bytes, const DecodePlan& plan, const Deco
   a.slot_mapping = l.slot_mapping;
   a.k_cache_w = (uint8_t*)l.k_cache;
   a.v_cache_w = (uint8_t*)l.v_cache;
+  a.prefix_plan = l.prefix_plan;
+  a.prefix_items = l.prefix_plan ? l.prefix_items : 0;
+  a.prefix_wgs = a.prefix_items * l.num_kv_heads;
+  // compacted units when several splits exist; the row walk of unit_of is
+  // bounded by nsplit
+  a.compact = l.batch > 1 && l.batch <= kMaxCompactBatch && plan.nsplit >= kMinCompactSplits &&
+              plan.nsplit <= kMaxCompactSplits && plan.split_tokens >= kMinCompactSplit;
+  a.sdiv = FastDiv((uint32_t)plan.split_tokens);
   return a;
 }
 
 hipError_t launch_decode_split(int elem_bytes, const DecodePlan& plan, const DecodeLaunch& l,
                                hipStream_t stream) {
   const DecodeArgs a = decode_args(elem_bytes, plan, l);
-  const int64_t grid = (int64_t)plan.nsplit * l.batch * l.num_kv_heads * plan.head_chunks;
+  const int64_t grid =
+      (int64_t)plan.nsplit * l.batch * l.num_kv_heads * plan.head_chunks + a.prefix_wgs;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (elem_bytes == 2)

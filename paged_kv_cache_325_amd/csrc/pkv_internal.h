@@ -81,7 +81,33 @@ struct DecodeLaunch {
   const void* v_new = nullptr;
   int64_t k_new_stride = 0, v_new_stride = 0;  // elements between sequences
   const int32_t* slot_mapping = nullptr;
+  // shared-prefix plan (device words, see below); nullptr: none
+  const int32_t* prefix_plan = nullptr;
+  int32_t prefix_items = 0;
 };
+
+// ---- shared-prefix decode plan ---------------------------------------------
+// Sequences whose block tables begin with the same physical blocks hold the
+// same K/V there; the plan names runs of such sequences ("subgroups") and the
+// leading splits they share, so that each shared split is attended once for
+// all members of its subgroup (one MFMA tile: up to 16 query columns, the
+// members' query heads of one kv head) and merged per sequence with its
+// private splits.  Device words (int32):
+//   [0] split length S the plan was built for, [1] items, [2] batch,
+//   [3] GQA group size G, [4] subgroups P;
+//   skip[batch]: leading splits of sequence b computed by its subgroup;
+//   P records of kPlanGroupWords: member count, kPlanMembers member ids;
+//   items x 2: subgroup, split.
+constexpr int kPlanHeader = 5;
+constexpr int kPlanMembers = 16;
+constexpr int kPlanGroupWords = 1 + kPlanMembers;
+
+int64_t prefix_plan_words_bound(int batch, int max_context_len, int split_tokens);
+// Builds the plan on the host; returns the number of words written, or -1
+// if `capacity` is too small.  *items receives the number of items.
+int64_t build_prefix_plan(const int32_t* block_tables, int max_blocks, const int32_t* context_lens,
+                          int batch, int block_size, int group, int split_tokens, int32_t* plan,
+                          int64_t capacity, int32_t* items);
 
 // The split kernel (partials, and outputs of single-split sequences) and the
 // merge kernel (outputs of split sequences).  Only q, caches, tables and
