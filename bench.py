@@ -265,6 +265,114 @@ def time_fused_step(d: Device, steps: int, warmup: int, torch):
     return eager_ms, wall, graph_ms
 
 
+def time_prefix_decode(d: Device, steps: int, warmup: int, torch):
+    """The shared-prefix decode of a workload whose tables share leading
+    blocks: the plan is built on the host from the host tables and lengths
+    (metadata, outside the timed region), then pkv_paged_decode_prefix (the
+    attention: split kernel with the plan's MFMA workgroups, and the merge)
+    and pkv_paged_decode_step_prefix (with the fused store) are each timed
+    ``steps`` times, MALL evicted before each, medians in ms.  None if the
+    plan shares nothing."""
+    import paged_kv_cache_325_amd as pkv
+
+    w = d.w
+    S = pkv.pkv_paged_decode_split_tokens(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                          w.max_context_len, w.block_size, 0)
+    plan, items = pkv.pkv_decode_prefix_plan(w.block_tables, w.context_lens, w.num_q_heads,
+                                             w.num_kv_heads, w.block_size, S)
+    if items == 0:
+        return None
+    plan = plan.cuda()
+
+    def attn():
+        pkv.pkv_paged_decode_prefix(d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens,
+                                    w.max_context_len, w.scale, plan, items, out=d.out,
+                                    workspace=d.workspace)
+
+    def step():
+        pkv.pkv_paged_decode_step_prefix(d.q, d.k, d.v, d.slot_mapping, d.k_cache, d.v_cache,
+                                         d.block_tables, d.context_lens, w.max_context_len,
+                                         w.scale, plan, items, out=d.out, workspace=d.workspace)
+
+    flush = make_flush(torch)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(max(warmup, 1)):
+            flush()
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for e0, e1 in evs:
+            flush()
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return median([e0.elapsed_time(e1) for e0, e1 in evs])
+
+    d.store()
+    out = {"items": items, "split_tokens": S, "attn_ms": timed(attn), "step_ms": timed(step)}
+    del flush
+    return out
+
+
+def prefix_sharing_study(torch, steps: int = 10, warmup: int = 3) -> dict:
+    """Where the shared-prefix decode pays: 64 sequences of 7000-9000 keys
+    (32 / 8 heads, bf16, 256-token blocks) whose first 6144 keys are shared
+    in groups of 4, i.e. 2.3x fewer distinct K/V bytes than logical ones.
+    The plain decode and the shared-prefix decode (attention calls), median
+    event-timed ms, MALL evicted before each."""
+    import numpy as np
+
+    import paged_kv_cache_325_amd as pkv
+    from workloads import Spec, build
+
+    rng = np.random.default_rng(325_600)
+    ctx = rng.integers(7000, 9000, size=64, endpoint=True).tolist()
+    w = build(Spec("decode-bf16-b64-ctx7000-9000-shared6144-groups4-h32-8", "decode", "bf16", 32,
+                   8, ctx, [1] * 64, 325_601, share_group=[b // 4 for b in range(64)],
+                   shared_blocks=[24] * 64))
+    d = Device(w, torch)
+    d.check()
+    d.store()
+    flush = make_flush(torch)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(warmup):
+            flush()
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for e0, e1 in evs:
+            flush()
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return median([e0.elapsed_time(e1) for e0, e1 in evs])
+
+    plain_ms = timed(lambda: pkv.pkv_paged_decode(d.q, d.k_cache, d.v_cache, d.block_tables,
+                                                  d.context_lens, w.max_context_len, w.scale,
+                                                  out=d.out, workspace=d.workspace))
+    pre = time_prefix_decode(d, steps, warmup, torch)
+    uniq = w.unique_kv_bytes() + w.qo_bytes()
+    logical = w.logical_kv_bytes() + w.qo_bytes()
+    res = {"workload": w.spec.name, "logical_bytes": logical, "unique_bytes": uniq,
+           "plain_decode_ms": round(plain_ms, 4),
+           "plain_unique_hbm_frac": round(uniq / (plain_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "prefix_items": pre["items"], "prefix_decode_ms": round(pre["attn_ms"], 4),
+           "prefix_unique_hbm_frac": round(uniq / (pre["attn_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                           4),
+           "prefix_fused_step_ms": round(pre["step_ms"], 4)}
+    del d, flush
+    torch.cuda.empty_cache()
+    return res
+
+
 def decode_batch_bucket(nb: int):
     """The first ``nb`` sequences of the 64-sequence decode workload (same
     lengths, seed and head counts): the batch of one graph bucket."""
@@ -333,20 +441,20 @@ def time_layer_stack(torch, w, layers: int = 28, reps: int = 20) -> dict:
 # changes, the figure no longer describes the kernel and is reported as null.
 TRAFFIC = {
     ("decode_split_kernel", "decode-bf16-b256-ctx1024-8192-h32-8"): {
-        "bytes": 4844590120, "source": "decode.hip",
-        "sha256": "3418e9720d115fe4854c31d3ac04f3a0bdc974d46f20d6525757db4113b7b29d"},
+        "bytes": 4844612284, "source": "decode.hip",
+        "sha256": "2716240162aa6dd2203cd22aa4c5cdff87922f76538e0089a45f0e3c8d632b5b"},
     ("decode_split_kernel", "decode-bf16-b64-ctx512-4096-h16-8"): {
-        "bytes": 545456801, "source": "decode.hip",
-        "sha256": "3418e9720d115fe4854c31d3ac04f3a0bdc974d46f20d6525757db4113b7b29d"},
+        "bytes": 545481660, "source": "decode.hip",
+        "sha256": "2716240162aa6dd2203cd22aa4c5cdff87922f76538e0089a45f0e3c8d632b5b"},
     ("decode_split_kernel", "decode-bf16-b16-lognormal8192-shared4096-h32-8"): {
-        "bytes": 620467092, "source": "decode.hip",
-        "sha256": "3418e9720d115fe4854c31d3ac04f3a0bdc974d46f20d6525757db4113b7b29d"},
+        "bytes": 610553422, "source": "decode.hip",
+        "sha256": "2716240162aa6dd2203cd22aa4c5cdff87922f76538e0089a45f0e3c8d632b5b"},
     ("decode_split_kernel", "decode-fp32-4seq"): {
-        "bytes": 9206271, "source": "decode.hip",
-        "sha256": "3418e9720d115fe4854c31d3ac04f3a0bdc974d46f20d6525757db4113b7b29d"},
+        "bytes": 9227881, "source": "decode.hip",
+        "sha256": "2716240162aa6dd2203cd22aa4c5cdff87922f76538e0089a45f0e3c8d632b5b"},
     ("prefill_kernel", "prefill-bf16-8seq-L1024-4096-prefix512-h32-8"): {
-        "bytes": 2076887192, "source": "prefill.hip",
-        "sha256": "80c6d337d028d260fd2ce99e992ec11b6f6be0e48a6f9b9dfa94afc69e46f88e"},
+        "bytes": 2076841180, "source": "prefill.hip",
+        "sha256": "c13f65d13d747ed016d32c9978e7eaddec58e1d0c1b1a5dddec22c38877f1ad0"},
 }
 
 
@@ -438,6 +546,8 @@ def measure(w, steps: int, warmup: int, torch, settle_s: float):
     if w.spec.mode == "decode":
         (r["fused_step_ms"], r["fused_wall_s"],
          r["fused_step_graph_ms"]) = time_fused_step(d, steps, warmup, torch)
+        if w.dtype == "bf16" and w.spec.share_group:
+            r["prefix"] = time_prefix_decode(d, steps, warmup, torch)
         attn_bytes = kv + w.qo_bytes()
         r["attn_bytes"] = attn_bytes
         r["unique_attn_bytes"] = w.unique_kv_bytes() + w.qo_bytes()
@@ -494,6 +604,14 @@ def summary(r) -> dict:
     if r["unique_attn_bytes"] != r["attn_bytes"]:
         e.update(decode_unique_gbs=round(r["unique_gbs"], 1),
                  decode_unique_hbm_frac=round(r["unique_gbs"] / HBM_PEAK_GBS, 4))
+    pre = r.get("prefix")
+    if pre:
+        ub = r["unique_attn_bytes"]
+        e.update(prefix_plan_items=pre["items"], prefix_decode_ms=round(pre["attn_ms"], 4),
+                 prefix_decode_unique_gbs=round(ub / (pre["attn_ms"] * 1e-3) / 1e9, 1),
+                 prefix_decode_unique_hbm_frac=round(ub / (pre["attn_ms"] * 1e-3) / 1e9
+                                                     / HBM_PEAK_GBS, 4),
+                 prefix_fused_step_ms=round(pre["step_ms"], 4))
     return e
 
 
@@ -819,6 +937,9 @@ def main() -> int:
         extra["block-size-study"] = time_block_sizes(torch)
         log("timing the host block manager")
         extra["block-manager-host"] = time_block_manager()
+        log("timing the shared-prefix decode on a heavily shared batch")
+        extra["prefix-sharing-study"] = prefix_sharing_study(torch)
+        log(f"prefix sharing: {extra['prefix-sharing-study']}")
 
     cpu = None
     if not args.no_cpu:

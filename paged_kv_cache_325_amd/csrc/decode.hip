@@ -789,29 +789,26 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 // M = max_s m_s, out = sum_s 2^(m_s-M) acc_s / sum_s 2^(m_s-M) l_s, with the
 // acc sum taken in split order.  The kernel is latency-bound (a few KB per
 // wavefront), so every load is issued before the first use: lane s fetches
-// split s's (m, l), and the acc rows of 16 splits are in flight while the
-// maximum is reduced.  Splits beyond 64 (very long contexts with small
-// splits) go through the general loop.  Sequences with a single split were
-// finished by the split kernel.
-template <int kElemBytes>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
-  constexpr int kBatch = 16;
+// split s's (m, l), and the acc rows of a batch of splits (4 or 16) are in
+// flight while the maximum is reduced.  Splits beyond 64 (very long
+// contexts with small splits) go through the general loop.  Sequences with
+// a single split were finished by the split kernel.
+//
+// merge_pair: one (sequence, query head) pair with ns splits, acc rows read
+// kBatch at a time (rows past the end are re-reads of the last row, with
+// weight 0).
+template <int kElemBytes, int kBatch>
+__device__ __forceinline__ void merge_pair(const DecodeArgs& a, int pair, int ns) {
   const int lane = threadIdx.x & 63;
-  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (pair >= a.batch * a.num_q_heads) return;
-  const int b = pair / a.num_q_heads;
-  const int n = a.context_lens[b];
-  const int ns = (n + a.split_tokens - 1) / a.split_tokens;
-  if (ns <= 1) return;
   const int64_t base = (int64_t)pair * a.nsplit;
   const float* acc_rows = a.ws_acc + base * kHeadDim + lane * 2;
 
-  // first group: (m, l) of splits 0..63 and acc rows of splits 0..15
+  // first group: (m, l) of splits 0..63 and acc rows of splits 0..kBatch-1
   f32x2 ml = f32x2{-INFINITY, 0.f};
   if (lane < ns) ml = *reinterpret_cast<const f32x2*>(a.ws_ml + (base + lane) * 2);
   f32x2 v[kBatch];
 #pragma unroll
-  for (int j = 0; j < kBatch; ++j)  // past the end: a valid row with weight 0
+  for (int j = 0; j < kBatch; ++j)
     v[j] = *reinterpret_cast<const f32x2*>(acc_rows + (int64_t)min(j, ns - 1) * kHeadDim);
 
   float M = ml[0];
@@ -855,6 +852,25 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     *reinterpret_cast<f32x2*>(a.out + (int64_t)pair * kRowBytes + lane * 8) =
         f32x2{o0 * inv, o1 * inv};
   }
+}
+
+// Pairs with at most 4 splits (long splits: the 256-sequence workload's
+// plan has 1-4 per sequence) take a 4-row batch: the load instructions of
+// the 16-row batch (12 of them re-reads) were what bounded that merge
+// (11.9 -> 8.6 us, bitwise equal; a path per power of two up to 32 cost
+// registers and occupancy and was slower).
+template <int kElemBytes>
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= a.batch * a.num_q_heads) return;
+  const int b = pair / a.num_q_heads;
+  const int n = a.context_lens[b];
+  const int ns = (n + a.split_tokens - 1) / a.split_tokens;
+  if (ns <= 1) return;
+  if (ns <= 4)
+    merge_pair<kElemBytes, 4>(a, pair, ns);
+  else
+    merge_pair<kElemBytes, 16>(a, pair, ns);
 }
 
 template <int kElemBytes, int kHeads, bool kSmall>
