@@ -453,8 +453,8 @@ TRAFFIC = {
         "bytes": 9227881, "source": "decode.hip",
         "sha256": "2716240162aa6dd2203cd22aa4c5cdff87922f76538e0089a45f0e3c8d632b5b"},
     ("prefill_kernel", "prefill-bf16-8seq-L1024-4096-prefix512-h32-8"): {
-        "bytes": 2076841180, "source": "prefill.hip",
-        "sha256": "c13f65d13d747ed016d32c9978e7eaddec58e1d0c1b1a5dddec22c38877f1ad0"},
+        "bytes": 2077070727, "source": "prefill.hip",
+        "sha256": "ac3ca31b791dc07406bda872e8460758b80ec5ed1a8544feaa6d1a49f7d45ed3"},
 }
 
 

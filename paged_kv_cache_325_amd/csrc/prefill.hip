@@ -191,10 +191,10 @@ __device__ __forceinline__ void phase_barrier() {
 
 // One work item: query tile r (counted from the end) of sequence b, kv head
 // g, head chunk hc, on 8 waves in two groups of 4 (see the kernel).
-// kBlock: the cache block size when it is fixed at compile time (256, the
-// pages' size: divisions become shifts), 0 for any other multiple of 64
-// (division by multiplication), -1 for blocks of 16 or 32 tokens (see
-// tile_offsets).
+// kBlock: the cache block size when it is fixed at compile time (a power of
+// two from 64 to 4096, 256 being the pages' size: divisions become shifts),
+// 0 for any other multiple of 64 (division by multiplication), -1 for
+// blocks of 16 or 32 tokens (see tile_offsets).
 template <int kBlock>
 __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4 (*kbuf)[kKT * 16],
                                              u32x4 (*vbuf)[kKT * 16]) {
@@ -656,13 +656,29 @@ hipError_t launch_prefill(const PrefillLaunch& l, hipStream_t stream) {
   a.k_row_stride = l.k_row_stride;
   a.v_row_stride = l.v_row_stride;
   a.bdiv = FastDiv((uint32_t)l.block_size);
-  if (a.cu_k || l.block_size == kBlockSize)  // contiguous keys use no block
-    hipLaunchKernelGGL(prefill_kernel<kBlockSize>, dim3((unsigned)grid), dim3(kThreads), 0,
-                       stream, a);
-  else if (l.block_size < kKT)  // 16 or 32
-    hipLaunchKernelGGL(prefill_kernel<-1>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(prefill_kernel<0>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  // Power-of-two block sizes are compile-time constants (divisions become
+  // shifts).  The runtime-size instantiation (kBlock = 0, other multiples of
+  // 64) is kept for the rest: the compiler's schedule of it has proved
+  // fragile -- small unrelated source changes made it drop the operand
+  // read-ahead of the tile loop (64- and 1024-token blocks 570 -> 650 us),
+  // while the compile-time instantiations keep it.
+  const dim3 g((unsigned)grid), t(kThreads);
+  if (a.cu_k) {  // contiguous keys use no block
+    hipLaunchKernelGGL(prefill_kernel<kBlockSize>, g, t, 0, stream, a);
+  } else {
+    switch (l.block_size) {
+      case 16:
+      case 32: hipLaunchKernelGGL(prefill_kernel<-1>, g, t, 0, stream, a); break;
+      case 64: hipLaunchKernelGGL(prefill_kernel<64>, g, t, 0, stream, a); break;
+      case 128: hipLaunchKernelGGL(prefill_kernel<128>, g, t, 0, stream, a); break;
+      case 256: hipLaunchKernelGGL(prefill_kernel<256>, g, t, 0, stream, a); break;
+      case 512: hipLaunchKernelGGL(prefill_kernel<512>, g, t, 0, stream, a); break;
+      case 1024: hipLaunchKernelGGL(prefill_kernel<1024>, g, t, 0, stream, a); break;
+      case 2048: hipLaunchKernelGGL(prefill_kernel<2048>, g, t, 0, stream, a); break;
+      case 4096: hipLaunchKernelGGL(prefill_kernel<4096>, g, t, 0, stream, a); break;
+      default: hipLaunchKernelGGL(prefill_kernel<0>, g, t, 0, stream, a); break;
+    }
+  }
   return hipGetLastError();
 }
 
