@@ -73,7 +73,10 @@ constexpr int kTargetWaves = 256 * 32;
 // 64- and 256-sequence workloads (16 splits of 256 keys, 4 of 2048) within
 // 0.5 %; 28-layer graph-replayed steps at batch 16 (8 splits of 512 keys)
 // 4 % slower, at batch 2-8 (64-256-key splits) unchanged -- hence the
-// bounds.  The row walk costs a ballot per row and 64 sequences.
+// bounds.  Putting the ragged last splits after all full ones took the
+// lognormal workload's decode from 124.1 to 119.5 us (bitwise equal); with
+// looser bounds (4 splits of 256 keys) the 64- and 256-sequence workloads
+// and batches 8-16 were 1-3 % slower.
 constexpr int kMaxCompactBatch = 256;
 constexpr int kMinCompactSplits = 16;
 constexpr int kMaxCompactSplits = 1024;
@@ -377,14 +380,15 @@ __device__ __forceinline__ void prefix_split(const DecodeArgs& a, int id, u32x4*
 // nsplit units per sequence, and for skewed lengths most of them are empty:
 // those workgroups, interleaved in the dispatch order, delayed the
 // workgroups of the long sequences' last splits and so stretched the tail.
-// Here unit u of the launch is the u-th (sequence, split) that has work
-// (split s of sequence b for lo_b <= s < hi_b, hi_b = max(1, ceil(n_b / S)):
-// one unit for an empty context, which writes its zero row; lo_b = the
-// splits a shared-prefix subgroup computes), in split-major order (so the
-// same split of different sequences runs together, as before); units past
-// the last one exit at the end of the dispatch.  Every lane holds the
-// counts of sequences lane + 64 k (batch <= 256, the host's condition);
-// each row s costs a ballot per k.  Returns false for a unit past the end.
+// Here unit u of the launch is the u-th (sequence, split) that has work:
+// first every full split (S keys) in split-major order (the same split of
+// different sequences runs together, as before), skipping the splits a
+// shared-prefix subgroup computes, then each sequence's ragged last split
+// (or the one unit of an empty context, which writes its zero row), the
+// shorter units at the end of the dispatch; units past the last one exit.
+// Every lane holds the counts of sequences lane + 64 k (batch <= 256, the
+// host's condition); each row s of the walk costs a ballot per k.  Returns
+// false for a unit past the end.
 template <bool kPrefix>
 __device__ __forceinline__ bool unit_of(const DecodeArgs& a, int u, int& b_out, int& s_out,
                                         int& n_out) {
@@ -397,24 +401,48 @@ __device__ __forceinline__ bool unit_of(const DecodeArgs& a, int u, int& b_out, 
     plan_ok = plan[0] == a.split_tokens && plan[1] == a.prefix_items && plan[2] == a.batch &&
               plan[3] == a.group;
   }
-  int nb[kMaxK], lo[kMaxK], hi[kMaxK];
-  int mine = 0;
+  // full splits lo .. full-1 first (split-major), then each sequence's
+  // ragged last split (or the zero row of an empty context) at s = full
+  int nb[kMaxK], lo[kMaxK], full[kMaxK];
+  bool rag[kMaxK];
+  int mine = 0, nrag = 0;
 #pragma unroll
   for (int k = 0; k < kMaxK; ++k) {
-    nb[k] = lo[k] = hi[k] = 0;
+    nb[k] = lo[k] = full[k] = 0;
+    rag[k] = false;
     if (k < K) {
       const int bb = lane + 64 * k;
       const bool in = bb < a.batch;
       nb[k] = in ? a.context_lens[bb] : 0;
-      hi[k] = in ? max(1, (int)a.sdiv.div((uint32_t)nb[k] + a.split_tokens - 1)) : 0;
+      full[k] = in ? (int)a.sdiv.div((uint32_t)nb[k]) : 0;
+      rag[k] = in && (nb[k] == 0 || nb[k] != full[k] * a.split_tokens);
       if constexpr (kPrefix)
-        lo[k] = (in && plan_ok) ? min(a.prefix_plan[kPlanHeader + bb], hi[k]) : 0;
-      mine += hi[k] - lo[k];
+        lo[k] = (in && plan_ok) ? min(a.prefix_plan[kPlanHeader + bb], full[k]) : 0;
+      mine += full[k] - lo[k];
+      nrag += rag[k] ? 1 : 0;
     }
   }
-  // units in all (exact in fp32: the host keeps batch * nsplit below 2^24);
-  // the units past the last one exit here
-  if ((float)u >= wave_sum((float)mine)) return false;
+  const int total1 = (int)wave_sum((float)mine);
+  if (u >= total1) {
+    int r = u - total1;
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) {
+      const uint64_t m = __builtin_amdgcn_ballot_w64(rag[k]);
+      const int c = __builtin_popcountll(m);
+      if (r >= 0 && r < c) {
+        const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(((m >> lane) & 1) && rank == r);
+        const int l = __builtin_ffsll((long long)hit) - 1;
+        b_out = 64 * k + l;
+        n_out = __builtin_amdgcn_readlane(nb[k], l);
+        s_out = __builtin_amdgcn_readlane(full[k], l);
+        return true;
+      }
+      r -= c;
+    }
+    return false;
+  }
   // walk the rows (splits) to the one holding unit u
   int before = 0;
   for (int s = 0; s < a.nsplit; ++s) {
@@ -424,7 +452,7 @@ __device__ __forceinline__ bool unit_of(const DecodeArgs& a, int u, int& b_out, 
     for (int k = 0; k < kMaxK; ++k) {
       m[k] = 0;
       if (k < K) {
-        m[k] = __builtin_amdgcn_ballot_w64(s >= lo[k] && s < hi[k]);
+        m[k] = __builtin_amdgcn_ballot_w64(s >= lo[k] && s < full[k]);
         row += __builtin_popcountll(m[k]);
       }
     }
@@ -434,7 +462,6 @@ __device__ __forceinline__ bool unit_of(const DecodeArgs& a, int u, int& b_out, 
       for (int k = 0; k < kMaxK; ++k) {
         const int c = __builtin_popcountll(m[k]);
         if (r >= 0 && r < c) {
-          // the lane of the r-th set bit of m[k]
           const int rank = __builtin_amdgcn_mbcnt_hi(
               (uint32_t)(m[k] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m[k], 0));
           const uint64_t hit = __builtin_amdgcn_ballot_w64(((m[k] >> lane) & 1) && rank == r);

@@ -95,6 +95,40 @@ def test_decode_more_than_64_splits():
     assert_close(out.to(torch.float64).cpu().numpy(), expected(w), "86 splits")
 
 
+# Compacted split units (the plan has >= 16 splits of >= 512 keys): lengths
+# on and off split multiples, an empty context, a context of 1, sequences
+# shorter than one split and one spanning all of them.  At 32 requested
+# splits of a 20 000-key context the plan has 27 splits of 768 keys.
+COMPACT_CTX = [20000, 0, 1, 767, 768, 769, 1536, 15360, 8193, 300, 0, 12000]
+
+
+@pytest.mark.parametrize("hq,hkv", [(16, 8), (8, 2)], ids=["g2", "g4"])
+def test_compacted_units_ragged_and_empty(hq, hkv):
+    spec = Spec(f"dec-compact-h{hq}-{hkv}", "decode", "bf16", hq, hkv, COMPACT_CTX,
+                [0 if c == 0 else 1 for c in COMPACT_CTX], 9211)
+    w = build(spec)
+    S = pkv.pkv_paged_decode_split_tokens(w.batch, hq, hkv, 128, w.max_context_len, 256, 32)
+    nsplit = -(-w.max_context_len // S)
+    assert S >= 512 and nsplit >= 16  # the compacted mode's bounds
+    d = to_device(w)
+    check_inputs(d)
+    k_pre, v_pre = d.k_cache.clone(), d.v_cache.clone()
+    announce(f"{spec.name}: fused step, compacted units")
+    out_step = pkv.pkv_paged_decode_step(d.q, d.k, d.v, d.slot_mapping, d.k_cache, d.v_cache,
+                                         d.block_tables, d.context_lens, w.max_context_len,
+                                         w.scale, num_splits=32)
+    d.k_cache.copy_(k_pre)
+    d.v_cache.copy_(v_pre)
+    d2, out = _run_step(w, num_splits=32)
+    torch.cuda.synchronize()
+    want = expected(w)
+    assert_close(out.to(torch.float64).cpu().numpy(), want, "compacted units")
+    assert torch.equal(out.view(torch.int16), out_step.view(torch.int16))
+    for b, c in enumerate(COMPACT_CTX):
+        if c == 0:
+            assert (out[b].float() == 0).all()
+
+
 @pytest.mark.parametrize("block_size", [256, 16, 64, 1024])
 def test_long_prefill_table_beyond_registers(block_size):
     # one 12 k-token sequence whose first 8 k tokens are cached: at 16-token
