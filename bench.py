@@ -441,17 +441,17 @@ def time_layer_stack(torch, w, layers: int = 28, reps: int = 20) -> dict:
 # changes, the figure no longer describes the kernel and is reported as null.
 TRAFFIC = {
     ("decode_split_kernel", "decode-bf16-b256-ctx1024-8192-h32-8"): {
-        "bytes": 4844612284, "source": "decode.hip",
-        "sha256": "2716240162aa6dd2203cd22aa4c5cdff87922f76538e0089a45f0e3c8d632b5b"},
+        "bytes": 4844623077, "source": "decode.hip",
+        "sha256": "2667b58d05dde644d9c9c484f61945536a090ead7a6a93db86393c559d9cecd4"},
     ("decode_split_kernel", "decode-bf16-b64-ctx512-4096-h16-8"): {
-        "bytes": 545481660, "source": "decode.hip",
-        "sha256": "2716240162aa6dd2203cd22aa4c5cdff87922f76538e0089a45f0e3c8d632b5b"},
+        "bytes": 545479848, "source": "decode.hip",
+        "sha256": "2667b58d05dde644d9c9c484f61945536a090ead7a6a93db86393c559d9cecd4"},
     ("decode_split_kernel", "decode-bf16-b16-lognormal8192-shared4096-h32-8"): {
-        "bytes": 610553422, "source": "decode.hip",
-        "sha256": "2716240162aa6dd2203cd22aa4c5cdff87922f76538e0089a45f0e3c8d632b5b"},
+        "bytes": 615870785, "source": "decode.hip",
+        "sha256": "2667b58d05dde644d9c9c484f61945536a090ead7a6a93db86393c559d9cecd4"},
     ("decode_split_kernel", "decode-fp32-4seq"): {
-        "bytes": 9227881, "source": "decode.hip",
-        "sha256": "2716240162aa6dd2203cd22aa4c5cdff87922f76538e0089a45f0e3c8d632b5b"},
+        "bytes": 9220715, "source": "decode.hip",
+        "sha256": "2667b58d05dde644d9c9c484f61945536a090ead7a6a93db86393c559d9cecd4"},
     ("prefill_kernel", "prefill-bf16-8seq-L1024-4096-prefix512-h32-8"): {
         "bytes": 2077070727, "source": "prefill.hip",
         "sha256": "ac3ca31b791dc07406bda872e8460758b80ec5ed1a8544feaa6d1a49f7d45ed3"},
