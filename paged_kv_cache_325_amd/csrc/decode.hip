@@ -526,16 +526,22 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   // writes).  The decode-step invariant makes this exactly store-then-decode:
   // the slot is -1 or the slot of position n-1, in a block no other
   // sequence reads.
+  // With 8 heads and blocks of 16 or 32 tokens the new row is not kept in
+  // registers through the loop (those 8 VGPRs would push the kernel past 256,
+  // one wave per SIMD instead of two): the last chunk reads it again from the
+  // input, where it is cache-resident.
+  constexpr bool kReloadNew = kHeads == 8 && kSmall;
+  auto new_row = [&](const uint8_t* base, int64_t stride) -> u32x4 {
+    return *reinterpret_cast<const u32x4*>(base + b * stride + (int64_t)g * S::kRowBytes +
+                                           (lane % kCPR) * 16);
+  };
   int slot_new = -1;
   u32x4 knew = u32x4{0u, 0u, 0u, 0u}, vnew = u32x4{0u, 0u, 0u, 0u};
   if constexpr (kFused) {
     slot_new = a.slot_mapping[b];
     if (slot_new >= 0) {
-      const int col_ = lane % kCPR;
-      knew = *reinterpret_cast<const u32x4*>(a.k_new + b * a.k_new_stride_bytes +
-                                             (int64_t)g * S::kRowBytes + col_ * 16);
-      vnew = *reinterpret_cast<const u32x4*>(a.v_new + b * a.v_new_stride_bytes +
-                                             (int64_t)g * S::kRowBytes + col_ * 16);
+      knew = new_row(a.k_new, a.k_new_stride_bytes);
+      vnew = new_row(a.v_new, a.v_new_stride_bytes);
       const int s_last = n > 0 ? (n - 1) / a.split_tokens : 0;
       if (hc == 0 && s == s_last && lane < kCPR) {
         const uint32_t p = a.bdiv.div((uint32_t)slot_new);
@@ -667,7 +673,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     // the fused store's row replaces the cache row (last chunk only; the
     // later LDS write of the same wave wins)
     const bool sub = !kPrefetch && p_new >= c0 && p_new < c0 + kTok;  // uniform
-    if (sub && lane < kCPR) k_lds[(p_new - c0) * (kCPR + 1) + lane] = knew;
+    if (sub && lane < kCPR)
+      k_lds[(p_new - c0) * (kCPR + 1) + lane] =
+          kReloadNew ? new_row(a.k_new, a.k_new_stride_bytes) : knew;
     __syncthreads();
     if constexpr (kPrefetch) {
       if constexpr (!kBounded) {
@@ -730,9 +738,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     __syncthreads();
 
     if (sub) {
+      const u32x4 vn = kReloadNew ? new_row(a.v_new, a.v_new_stride_bytes) : vnew;
 #pragma unroll
       for (int i = 0; i < S::kLoads; ++i)
-        if (i * S::kRowsPerLoad + grp == p_new - c0) vr[i] = vnew;
+        if (i * S::kRowsPerLoad + grp == p_new - c0) vr[i] = vn;
     }
     // PV: lane holds kVec dims (column col) of tokens i*kRowsPerLoad + grp
 #pragma unroll

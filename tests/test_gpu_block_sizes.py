@@ -60,12 +60,15 @@ def test_block_size_against_oracle(spec, B):
 
 
 @pytest.mark.parametrize("B", [16, 32, 512])
-def test_fused_step_at_block_size(B):
-    spec = [s for s in small_specs() if s.name == "dec-bf16-g2-ragged"][0]
+@pytest.mark.parametrize("name", ["dec-bf16-g2-ragged", "dec-bf16-g8"])
+def test_fused_step_at_block_size(name, B):
+    # dec-bf16-g8: 8 query heads per workgroup, whose fused kernel at blocks
+    # of 16 or 32 tokens reads the new row again in its last chunk
+    spec = [s for s in small_specs() if s.name == name][0]
     w = build(at_block_size(spec, B))
     a, b = to_device(w), to_device(w)
     check_inputs(a)
-    announce(f"fused step at block size {B}")
+    announce(f"fused step at block size {B}: {name}")
     store(a)
     ref_out = attend(a)
     out = pkv.pkv_paged_decode_step(b.q, b.k, b.v, b.slot_mapping, b.k_cache, b.v_cache,

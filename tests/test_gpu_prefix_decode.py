@@ -66,6 +66,9 @@ CASES = [
     # G = 8: runs of 2; a class of 5 -> 2 + 2 + (1 dropped)
     (_spec("pfx-g8", 8, 1, [2000, 2100, 1900, 2500, 2222, 3000],
            [0, 0, 0, 0, 0, -1], [6, 6, 6, 6, 6, 0], 9704), [0, 12]),
+    # G = 8 with 16-token blocks (the fused kernel re-reads the new row)
+    (_spec("pfx-g8-b16", 8, 1, [1300, 1250, 1400, 1100], [0, 0, 1, 1], [50, 50, 40, 40], 9708,
+           block_size=16), [0, 6]),
     # 32-token blocks and 64-token blocks
     (_spec("pfx-g4-b32", 8, 2, [1100, 1000, 1200, 600], [0, 0, 0, -1], [20, 20, 20, 0], 9705,
            block_size=32), [0, 5]),
