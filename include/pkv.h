@@ -40,7 +40,10 @@
  * blocks of any supported size give bitwise the same results (when the
  * decode split plan is the same, see pkv_paged_decode_split_tokens).
  *
- * GQA: query head h reads kv head h / (num_q_heads / num_kv_heads).
+ * GQA: query head h reads kv head h / (num_q_heads / num_kv_heads); any
+ * group size is served (decode workgroups take 1, 2, 4 or 8 query heads of a
+ * group, the unused ones of a last, partial chunk masked; prefill work items
+ * take 4, 2 or 1 heads, whichever divides the group).
  * Attention: out = sum_j softmax_j(scale * q . k_j) v_j over the visible keys,
  * fp32 accumulation, output in the input element type (bf16 rounded to
  * nearest even).  A query with no visible key gets a zero output row.
@@ -52,9 +55,7 @@
  *                        max_context_len > max_blocks_per_seq * block_size,
  *                        causal != 1, a scale that is not finite (NaN, +-inf);
  *   PKV_ERR_UNSUPPORTED  a block_size outside {16, 32, 64 k <= 4096},
- *                        head_dim != 128, a GQA group size
- *                        not in {1, 2, 4, 8} and not a multiple of 8, fp32
- *                        prefill;
+ *                        head_dim != 128, fp32 prefill;
  *   PKV_ERR_WORKSPACE    decode workspace smaller than required;
  *   PKV_ERR_HIP          a HIP launch reported an error.
  * A zero count (no tokens, empty batch) returns PKV_OK and launches nothing.

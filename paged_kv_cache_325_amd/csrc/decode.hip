@@ -518,6 +518,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   }
   const int start = s * a.split_tokens;
   const int h0 = g * a.group + hc * kHeads;
+  // query heads of this chunk that exist: fewer than kHeads in the last
+  // chunk when the group is not a multiple of kHeads (the rest compute on a
+  // zero q and write nothing)
+  const int nh = min(kHeads, a.group - hc * kHeads);
 
   // Fused store: the workgroup of head chunk 0 whose split holds the last
   // position writes the new row of kv head g to its slot, and every
@@ -562,7 +566,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   }
   if (start >= n) {
     if (s == 0) {  // empty context: zero output rows
-      for (int i = lane; i < kHeads * kCPR; i += 64) {
+      for (int i = lane; i < nh * kCPR; i += 64) {
         const int h = i / kCPR, c = i % kCPR;
         uint8_t* o = a.out + ((int64_t)b * a.num_q_heads + h0 + h) * S::kRowBytes + c * 16;
         *reinterpret_cast<u32x4*>(o) = u32x4{0u, 0u, 0u, 0u};
@@ -576,8 +580,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   // query rows of the heads handled here -> LDS
   for (int i = lane; i < kHeads * kCPR; i += 64) {
     const int h = i / kCPR, c = i % kCPR;
-    q_lds[i] = *reinterpret_cast<const u32x4*>(a.q + b * a.q_stride_bytes +
-                                                (int64_t)(h0 + h) * S::kRowBytes + c * 16);
+    q_lds[i] = h < nh ? *reinterpret_cast<const u32x4*>(a.q + b * a.q_stride_bytes +
+                                                         (int64_t)(h0 + h) * S::kRowBytes + c * 16)
+                      : u32x4{0u, 0u, 0u, 0u};
   }
 
   float m[kHeads], lsum[kHeads], acc[kHeads][kVec];
@@ -790,6 +795,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     if (lane < kCPR) {
 #pragma unroll
       for (int h = 0; h < kHeads; ++h) {
+        if (h >= nh) break;
         const float inv = 1.0f / lsum[h];
         uint8_t* o = a.out + ((int64_t)b * a.num_q_heads + h0 + h) * S::kRowBytes + col * 16;
         u32x4 w;
@@ -810,6 +816,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   if (lane < kCPR) {
 #pragma unroll
     for (int h = 0; h < kHeads; ++h) {
+      if (h >= nh) break;
       const int64_t slot = ((int64_t)b * a.num_q_heads + h0 + h) * a.nsplit + s;
       float* dst = a.ws_acc + slot * kHeadDim + col * kVec;
 #pragma unroll
@@ -950,10 +957,16 @@ void launch_split_heads(int heads, const DecodeArgs& args, unsigned grid, hipStr
 
 }  // namespace
 
+// Query heads per workgroup: the group itself when it is 1, 2, 4 or 8;
+// otherwise the next of those sizes (8 for groups above 8), the heads past
+// the group masked in the last chunk -- each workgroup still reads its kv
+// head's K/V once for all the heads it serves.
 int decode_heads_per_wg(int group) {
-  if (group == 1 || group == 2 || group == 4 || group == 8) return group;
-  if (group > 8 && group % 8 == 0) return 8;
-  return 0;
+  if (group < 1) return 0;
+  if (group >= 8) return 8;
+  int h = 1;
+  while (h < group) h <<= 1;
+  return h;
 }
 
 bool plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_context_len,
@@ -963,7 +976,7 @@ bool plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_context_l
   if (hpw == 0) return false;
   plan->group = group;
   plan->heads_per_wg = hpw;
-  plan->head_chunks = group / hpw;
+  plan->head_chunks = (group + hpw - 1) / hpw;
   const int64_t units = (int64_t)batch * num_kv_heads * plan->head_chunks;
   const int max_chunks = max_context_len > 0 ? (max_context_len + 63) / 64 : 1;
   int64_t want;

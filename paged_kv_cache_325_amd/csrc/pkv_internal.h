@@ -53,7 +53,7 @@ int decode_heads_per_wg(int group);
 struct DecodePlan {
   int group;         // Hq / Hkv
   int heads_per_wg;  // 1, 2, 4 or 8
-  int head_chunks;   // group / heads_per_wg
+  int head_chunks;   // ceil(group / heads_per_wg)
   int split_tokens;  // keys per split, multiple of 64
   int nsplit;        // ceil(max_context_len / split_tokens), >= 1
   size_t workspace_bytes;

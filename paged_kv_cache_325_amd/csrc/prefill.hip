@@ -19,8 +19,9 @@
 //
 // Work decomposition.  A work item is 8 wavefronts x 32 query rows of one
 // kv head g of one sequence: 4 query heads of g's group x 64 positions
-// (group >= 4), 2 heads x 128 positions (group 2) or 1 head x 256 positions
-// (group 1).  All 8 waves share every K/V tile the workgroup stages.  Keys
+// (group a multiple of 4), 2 heads x 128 positions (other even groups) or
+// 1 head x 256 positions (odd groups).  All 8 waves share every K/V tile the
+// workgroup stages.  Keys
 // are processed in tiles of 64 (a tile never crosses a 256-token block, so
 // one block-table entry per tile; the item's entries are loaded once).
 // Items are numbered last-query-tile first (most keys first) and handed
@@ -597,7 +598,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 
 }  // namespace
 
-bool prefill_supported_group(int group) { return group == 1 || group == 2 || group % 4 == 0; }
+bool prefill_supported_group(int group) { return group >= 1; }
 
 // CUs of the current device, cached per device (the grid of the persistent
 // kernel is one workgroup per CU).
@@ -631,7 +632,8 @@ hipError_t launch_prefill(const PrefillLaunch& l, hipStream_t stream) {
   a.num_q_heads = l.num_q_heads;
   a.num_kv_heads = l.num_kv_heads;
   a.group = l.num_q_heads / l.num_kv_heads;
-  a.heads_per_wg = a.group >= 4 ? 4 : a.group;
+  // the largest of 4, 2, 1 that divides the group
+  a.heads_per_wg = a.group % 4 == 0 ? 4 : a.group % 2 == 0 ? 2 : 1;
   a.pos_tiles = kWaves / a.heads_per_wg;
   a.head_chunks = a.group / a.heads_per_wg;
   const int wg_rows = kQT * a.pos_tiles;

@@ -109,7 +109,7 @@ def test_decode_step_errors():
     assert _step(ks=8 * 128 - 8) == INVALID   # stride below a row
     assert _step(vs=8 * 128 + 3) == INVALID   # stride not a whole 16-byte chunk
     assert _step(nblk=0) == INVALID
-    assert _step(hq=24) == UNSUPPORTED
+    assert _step(hq=24, batch=0) == OK  # group of 3: served (nothing to do)
     assert _step(ws=None, wsb=0) == WORKSPACE
     assert "k_new" in (_step(kn=None) and pkv.pkv_last_error())
 
@@ -140,7 +140,7 @@ def test_decode_errors():
     assert _decode(batch=0) == OK
     assert _decode(batch=-1) == INVALID
     assert _decode(hq=12) == INVALID  # 12 % 8
-    assert _decode(hq=24) == UNSUPPORTED  # group of 3
+    assert _decode(hq=24, batch=0) == OK  # group of 3: served (nothing to do)
     assert _decode(hq=0) == INVALID
     assert _decode(d=256) == UNSUPPORTED
     assert _decode(bs=48) == UNSUPPORTED
@@ -204,7 +204,7 @@ def test_prefill_errors():
     assert _prefill(maxq=0) == OK
     assert _prefill(causal=0) == INVALID
     assert _prefill(dtype=FP32) == UNSUPPORTED
-    assert _prefill(hq=24) == UNSUPPORTED  # group of 3
+    assert _prefill(hq=24, batch=0) == OK  # group of 3: served (nothing to do)
     assert _prefill(d=64) == UNSUPPORTED
     assert _prefill(maxctx=5 * 256) == INVALID
     assert _prefill(cu=None) == INVALID
@@ -235,7 +235,7 @@ def test_prefill_contiguous_errors():
     assert _prefill_contig(maxq=0) == OK
     assert _prefill_contig(causal=0) == INVALID
     assert _prefill_contig(dtype=FP32) == UNSUPPORTED
-    assert _prefill_contig(hq=24) == UNSUPPORTED
+    assert _prefill_contig(hq=24, batch=0) == OK  # group of 3: served
     assert _prefill_contig(cuk=None) == INVALID
     assert _prefill_contig(k=FAKE + 2) == INVALID
     assert _prefill_contig(ks=8 * 128 - 8) == INVALID
@@ -281,7 +281,7 @@ def test_merge_errors():
     assert _merge(out=None) == INVALID
     assert _merge(ws=None, wsb=0) == WORKSPACE
     assert _merge(d=64) == UNSUPPORTED
-    assert _merge(hq=24) == UNSUPPORTED
+    assert _merge(hq=24, batch=0) == OK  # group of 3: served
     assert _merge(splits=-1) == INVALID
     assert _merge(dtype=9) == INVALID
 

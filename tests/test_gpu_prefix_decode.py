@@ -66,6 +66,9 @@ CASES = [
     # G = 8: runs of 2; a class of 5 -> 2 + 2 + (1 dropped)
     (_spec("pfx-g8", 8, 1, [2000, 2100, 1900, 2500, 2222, 3000],
            [0, 0, 0, 0, 0, -1], [6, 6, 6, 6, 6, 0], 9704), [0, 12]),
+    # G = 5: runs of 3 (15 of the 16 columns)
+    (_spec("pfx-g5", 10, 2, [1800, 1900, 2000, 1700, 2100], [0, 0, 0, 1, 1], [5, 5, 5, 4, 4],
+           9709), [0, 9]),
     # G = 8 with 16-token blocks (the fused kernel re-reads the new row)
     (_spec("pfx-g8-b16", 8, 1, [1300, 1250, 1400, 1100], [0, 0, 1, 1], [50, 50, 40, 40], 9708,
            block_size=16), [0, 6]),

@@ -384,7 +384,7 @@ def config(index: int) -> Workload:
 
 def small_specs():
     """Parity cases the oracle finishes in seconds: several 64-token chunks,
-    several blocks, ragged tails, GQA 1/2/4/8, fp32 and bf16, contexts of 1,
+    several blocks, ragged tails, GQA 1/2/3/4/5/6/8/12, fp32 and bf16, contexts of 1,
     an empty context, prefill sequences without query rows, shared prefixes,
     skipped stores and extra padding."""
     out = []
@@ -400,12 +400,23 @@ def small_specs():
                     share_group=[0, 0, 1, 1], shared_blocks=[4, 2, 4, 1]))
     out.append(Spec("dec-bf16-peaked", "decode", "bf16", 8, 2, [2000, 517, 64], [1] * 3, 9007, q_scale=6.0))
     out.append(Spec("dec-bf16-empty-ctx", "decode", "bf16", 4, 2, [0, 33, 0], [0, 1, 0], 9008))
+    # GQA groups that are not 1, 2, 4 or 8: a masked head in the workgroup
+    # (3 of 4, 5 of 8), a partial second chunk (12 = 8 + 4), fp32 with 6 of 8
+    out.append(Spec("dec-bf16-g3", "decode", "bf16", 6, 2, [1000, 65, 1], [1] * 3, 9009))
+    out.append(Spec("dec-bf16-g5", "decode", "bf16", 10, 2, [2100, 300], [1] * 2, 9010))
+    out.append(Spec("dec-bf16-g12", "decode", "bf16", 12, 1, [700, 1500], [1] * 2, 9011))
+    out.append(Spec("dec-fp32-g6", "decode", "fp32", 6, 1, [400, 33], [1] * 2, 9012))
     out.append(Spec("pre-bf16-g4", "prefill", "bf16", 8, 2, [300, 512 + 37, 256 + 1, 1024 + 700],
                     [300, 37, 1, 700], 9101, share_group=[-1, 0, 0, 0], shared_blocks=[0, 2, 1, 4]))
     out.append(Spec("pre-bf16-g2", "prefill", "bf16", 4, 2, [63, 64, 65, 129, 600],
                     [63, 64, 65, 129, 88], 9102))
     out.append(Spec("pre-bf16-g8", "prefill", "bf16", 8, 1, [200, 777], [200, 500], 9103))
     out.append(Spec("pre-bf16-peaked", "prefill", "bf16", 8, 2, [900, 300], [400, 300], 9104, q_scale=6.0))
+    # odd and non-multiple-of-4 groups: 1 head x 256 positions per work
+    # item (3, 5), 2 heads x 128 positions (6)
+    out.append(Spec("pre-bf16-g3", "prefill", "bf16", 6, 2, [300, 700], [300, 450], 9106))
+    out.append(Spec("pre-bf16-g5", "prefill", "bf16", 5, 1, [520, 129], [400, 129], 9107))
+    out.append(Spec("pre-bf16-g6", "prefill", "bf16", 12, 2, [333, 640], [333, 200], 9108))
     # sequences with cached context but no query rows this step, first and
     # in the middle, beside a single-row and a short fresh prompt
     out.append(Spec("pre-bf16-zero-rows", "prefill", "bf16", 8, 2, [300, 5, 700, 256],
