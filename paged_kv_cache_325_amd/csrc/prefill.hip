@@ -356,25 +356,30 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4
   u32x4 pfrag[4];  // B operands of the PV product: (kt, ks) -> 16 keys
 
   // ---- S^T = K Q^T for the 64 keys of tile t --------------------------------
+  // MFMA i = (kb, kt) = (i / 2, i % 2).  The operand reads run six MFMAs
+  // ahead in a fixed order, fenced by sched_barrier: left to the scheduler,
+  // the read-ahead came and went with unrelated source changes (and with it
+  // an lgkmcnt(0) wait before every MFMA).
   auto scores = [&](int t) {
     const u32x4* kb_ = kbuf[t % kSlots];
+    constexpr int kAheadS = 6;
+    u32x4 opnd[16];
+    auto rd = [&](int i) {
+      const int kb = i >> 1, kt = i & 1;
+      const int key = kt * 32 + j;
+      opnd[i] = kb_[key * 16 + k_pos(key, kb * 2 + hf)];
+    };
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb)
+    for (int i = 0; i < kAheadS; ++i) rd(i);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const int key = kt * 32 + j;
-        const u32x4 av = kb_[key * 16 + k_pos(key, kb * 2 + hf)];
-        s_acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            as_bf16x8(av), as_bf16x8(qreg[kb]), kb == 0 ? f32x16{} : s_acc[kt], 0, 0, 0);
-      }
-    // operand reads run six MFMAs ahead (4 and 8 measured the same)
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-    for (int i = 0; i < 10; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int i = 0; i < 16; ++i) {
+      const int kb = i >> 1, kt = i & 1;
+      s_acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          as_bf16x8(opnd[i]), as_bf16x8(qreg[kb]), kb == 0 ? f32x16{} : s_acc[kt], 0, 0, 0);
+      if (i + kAheadS < 16) rd(i + kAheadS);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
   };
 
   // ---- online softmax (base 2) of tile t -> pfrag --------------------------
@@ -445,33 +450,32 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4
   };
 
   // ---- O^T += V^T P^T for tile t ---------------------------------------------
+  // MFMA i = (db, kt, ks) = (i / 4, (i / 2) % 2, i % 2); its A operand is two
+  // transpose reads.  The reads run five MFMAs ahead in a fixed order, as in
+  // the scores above.
   auto pv = [&](int t) {
     const u32x4* vb = vbuf[t % kSlots];
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    constexpr int kAheadP = 5;
+    u32x4 opnd[16];
+    auto rd = [&](int i) {
+      const int db = i >> 2, kt = (i >> 1) & 1, ks = i & 1;
       const int dim = db * 32 + 16 * (tr_g & 1) + 4 * tr_a;
+      const int key = kt * 32 + ks * 16 + 4 * hf + tr_m;
+      const uint64_t lo = tr_read(vb, key, dim);
+      const uint64_t hi = tr_read(vb, key + 8, dim);
+      opnd[i] = u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+    };
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+    for (int i = 0; i < kAheadP; ++i) rd(i);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int key = kt * 32 + ks * 16 + 4 * hf + tr_m;
-          const uint64_t lo = tr_read(vb, key, dim);
-          const uint64_t hi = tr_read(vb, key + 8, dim);
-          const u32x4 av = u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi,
-                                 (uint32_t)(hi >> 32)};
-          o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              as_bf16x8(av), as_bf16x8(pfrag[kt * 2 + ks]), o_acc[db], 0, 0, 0);
-        }
+    for (int i = 0; i < 16; ++i) {
+      const int db = i >> 2, kt = (i >> 1) & 1, ks = i & 1;
+      o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          as_bf16x8(opnd[i]), as_bf16x8(pfrag[kt * 2 + ks]), o_acc[db], 0, 0, 0);
+      if (i + kAheadP < 16) rd(i + kAheadP);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // operand reads (two per MFMA) run five MFMAs ahead (3 and 7 measured
-    // the same)
-    __builtin_amdgcn_sched_group_barrier(0x100, 10, 1);
-#pragma unroll
-    for (int i = 0; i < 11; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 5, 1);
   };
 
   // ---- ping-pong schedule ------------------------------------------------------
@@ -659,11 +663,8 @@ hipError_t launch_prefill(const PrefillLaunch& l, hipStream_t stream) {
   a.v_row_stride = l.v_row_stride;
   a.bdiv = FastDiv((uint32_t)l.block_size);
   // Power-of-two block sizes are compile-time constants (divisions become
-  // shifts).  The runtime-size instantiation (kBlock = 0, other multiples of
-  // 64) is kept for the rest: the compiler's schedule of it has proved
-  // fragile -- small unrelated source changes made it drop the operand
-  // read-ahead of the tile loop (64- and 1024-token blocks 570 -> 650 us),
-  // while the compile-time instantiations keep it.
+  // shifts); the runtime-size instantiation (kBlock = 0) serves the other
+  // multiples of 64.
   const dim3 g((unsigned)grid), t(kThreads);
   if (a.cu_k) {  // contiguous keys use no block
     hipLaunchKernelGGL(prefill_kernel<kBlockSize>, g, t, 0, stream, a);
