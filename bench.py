@@ -441,20 +441,20 @@ def time_layer_stack(torch, w, layers: int = 28, reps: int = 20) -> dict:
 # changes, the figure no longer describes the kernel and is reported as null.
 TRAFFIC = {
     ("decode_split_kernel", "decode-bf16-b256-ctx1024-8192-h32-8"): {
-        "bytes": 4844623077, "source": "decode.hip",
-        "sha256": "2667b58d05dde644d9c9c484f61945536a090ead7a6a93db86393c559d9cecd4"},
+        "bytes": 4844628730, "source": "decode.hip",
+        "sha256": "5ee831548692cf55da7dd9962dbcd5155c713c0c1c859ffccb8694cad34015c9"},
     ("decode_split_kernel", "decode-bf16-b64-ctx512-4096-h16-8"): {
-        "bytes": 545479848, "source": "decode.hip",
-        "sha256": "2667b58d05dde644d9c9c484f61945536a090ead7a6a93db86393c559d9cecd4"},
+        "bytes": 545473810, "source": "decode.hip",
+        "sha256": "5ee831548692cf55da7dd9962dbcd5155c713c0c1c859ffccb8694cad34015c9"},
     ("decode_split_kernel", "decode-bf16-b16-lognormal8192-shared4096-h32-8"): {
-        "bytes": 615870785, "source": "decode.hip",
-        "sha256": "2667b58d05dde644d9c9c484f61945536a090ead7a6a93db86393c559d9cecd4"},
+        "bytes": 614320516, "source": "decode.hip",
+        "sha256": "5ee831548692cf55da7dd9962dbcd5155c713c0c1c859ffccb8694cad34015c9"},
     ("decode_split_kernel", "decode-fp32-4seq"): {
-        "bytes": 9220715, "source": "decode.hip",
-        "sha256": "2667b58d05dde644d9c9c484f61945536a090ead7a6a93db86393c559d9cecd4"},
+        "bytes": 9229820, "source": "decode.hip",
+        "sha256": "5ee831548692cf55da7dd9962dbcd5155c713c0c1c859ffccb8694cad34015c9"},
     ("prefill_kernel", "prefill-bf16-8seq-L1024-4096-prefix512-h32-8"): {
-        "bytes": 2077070727, "source": "prefill.hip",
-        "sha256": "ac3ca31b791dc07406bda872e8460758b80ec5ed1a8544feaa6d1a49f7d45ed3"},
+        "bytes": 2068378548, "source": "prefill.hip",
+        "sha256": "5b1786f6a5dfd25ce2425141c2bf9c994e178782b8660d8820a87f226612c4db"},
 }
 
 
