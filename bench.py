@@ -39,7 +39,9 @@ launched eagerly and replayed from one captured graph
 (``decode-step-28-layers``; the 4-sequence fp32 workload, batches of 1, 4
 and 16 of the 64-sequence workload's sequences, and all 64), the 64-sequence
 decode and the prefill with cache blocks of 16, 32, 64 and 1024 tokens
-(``block-size-study``: attention time and fragmentation), and the host time
+(``block-size-study``: attention time and fragmentation), the 256-sequence
+and long-context decode and the prefill at one GPU's share of 8-way tensor
+parallelism (4 query heads, 1 kv head; ``tp8-per-rank``), and the host time
 of the block manager (C++ through the binding) for one decode step of 256
 sequences and one prefill admission of 8 prompts; the oracle's time for the
 same appears under ``cpu_baseline.block_manager``.
@@ -744,6 +746,40 @@ def time_block_sizes(torch, steps: int = 10, warmup: int = 3) -> dict:
     return out
 
 
+def time_per_rank_shapes(torch, steps: int = 10, warmup: int = 3) -> dict:
+    """One GPU's share under 8-way tensor parallelism (heads split over the
+    GPUs, 32/8 -> 4 query heads and 1 kv head per GPU; tables, lengths and
+    slots replicated): the 256-sequence and the long-context decode and the
+    prefill workload drawn with those head counts, attention timed as in
+    time_steps."""
+    import dataclasses
+
+    from workloads import build, config_specs
+
+    out = {}
+    for index in (4, 5, 3):
+        spec, rng = config_specs(index)
+        w = build(dataclasses.replace(spec, name=f"{spec.name}-tp8-rank", num_q_heads=4,
+                                      num_kv_heads=1), rng)
+        d = Device(w, torch)
+        d.check()
+        _, part_ms, _ = time_steps(d, steps, warmup, torch, 0.3)
+        attn_ms = median([sum(x) for x in zip(*part_ms)])
+        e = {"attn_ms": round(attn_ms, 4)}
+        if w.spec.mode == "decode":
+            gbs = (w.logical_kv_bytes() + w.qo_bytes()) / (attn_ms * 1e-3) / 1e9
+            e.update(decode_gbs=round(gbs, 1), decode_hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
+                     partials_ms=round(median(part_ms[0]), 4))
+        else:
+            tf = w.prefill_flops() / (attn_ms * 1e-3) / 1e12
+            e.update(prefill_tflops=round(tf, 1), mfma_frac=round(tf / MFMA_BF16_PEAK_TFLOPS, 4))
+        out[w.spec.name] = e
+        log(f"per-rank shape, workload {index}: {e}")
+        del d
+        torch.cuda.empty_cache()
+    return out
+
+
 # Host block manager: one engine step's bookkeeping at the shapes of the
 # 256-sequence decode workload (contexts U[1024, 8192]) and of the prefill
 # workload (8 prompts of U[1024, 4096] tokens behind a shared 512-token
@@ -935,6 +971,8 @@ def main() -> int:
         log(f"28-layer decode step: {extra['decode-step-28-layers']}")
         log("timing other cache block sizes")
         extra["block-size-study"] = time_block_sizes(torch)
+        log("timing one GPU's share of 8-way tensor parallelism")
+        extra["tp8-per-rank"] = time_per_rank_shapes(torch)
         log("timing the host block manager")
         extra["block-manager-host"] = time_block_manager()
         log("timing the shared-prefix decode on a heavily shared batch")
