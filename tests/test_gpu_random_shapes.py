@@ -3,9 +3,14 @@ prefill), the dtype, the GQA group (odd and above 8 included), the cache
 block size, the batch, ragged and empty lengths, shared prefixes, skipped
 stores, table padding, the softmax scale (negative and zero included) and
 the decode split count from its seed, then checks the store bit-exact and
-attention against the CPU oracle within the parity tolerance (and, for
-decode batches where every sequence stores a token, the one-call fused step
-bitwise against the two calls).  The fixed cases elsewhere cover each
+attention against the CPU oracle within the parity tolerance.  Decode
+batches where every sequence stores a token also run the one-call fused
+step (bitwise the two calls); prefill cases also run the prefill over the
+same keys gathered into contiguous rows (bitwise the paged prefill).  A
+second set draws batches whose tables share prefix blocks in several
+classes and runs the shared-prefix decode with the host planner's plan (the
+plan word for word against the oracle's, attention against the oracle, the
+fused form bitwise the two-call form).  The fixed cases elsewhere cover each
 feature on its own; these cover them in combination."""
 
 from __future__ import annotations
@@ -15,6 +20,7 @@ import pytest
 import torch
 
 import paged_kv_cache_325_amd as pkv
+from oracle import prefix_plan as pp
 from tests.gpu_helpers import announce, assert_close, attend, check_inputs, store, to_device
 from tests.oracle_helpers import expected, stored_bits
 from workloads import Spec, bits_view, build
@@ -109,3 +115,91 @@ def test_random_shape_against_oracle(seed):
         torch.cuda.synchronize()
         assert torch.equal(fused.view(torch.int8), out.view(torch.int8)), "fused step differs"
         assert torch.equal(e.k_cache.view(torch.int8), d.k_cache.view(torch.int8))
+
+    if spec.mode == "prefill":
+        # the same keys as contiguous rows, gathered from the post-store cache
+        blk, row = [], []
+        for b in range(w.batch):
+            j = np.arange(int(w.context_lens[b]))
+            blk.append(w.block_tables[b][j // w.block_size])
+            row.append(j % w.block_size)
+        blk = torch.from_numpy(np.concatenate(blk).astype(np.int64)).cuda()
+        row = torch.from_numpy(np.concatenate(row).astype(np.int64)).cuda()
+        k = d.k_cache[blk, :, row, :].contiguous()
+        v = d.v_cache[blk, :, row, :].contiguous()
+        cu_k = np.concatenate([[0], np.cumsum(w.context_lens)]).astype(np.int32)
+        announce(f"{spec.name}: contiguous prefill")
+        contig = pkv.pkv_prefill_varlen(d.q, k, v, d.cu_seqlens_q, torch.from_numpy(cu_k).cuda(),
+                                        w.max_seqlen_q, w.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(contig.view(torch.int16), out.view(torch.int16)), "contiguous differs"
+
+
+def random_prefix_spec(seed: int) -> tuple[Spec, int]:
+    """A random decode batch (bf16) whose sequences fall into sharing
+    classes: each class shares its first blocks (per member, between one and
+    all the blocks before the member's new token), plus a few unshared
+    sequences; and the split count (0: the automatic plan)."""
+    r = np.random.default_rng(34_500 + seed)
+    group = int(r.choice([1, 2, 3, 4, 5, 6, 8]))
+    hkv = int(r.choice([1, 2]))
+    B = int(r.choice([16, 32, 64, 128, 256, 512]))
+    classes = int(r.integers(1, 4))
+    ctx, groups = [], []
+    for c in range(classes):
+        members = int(r.integers(2, 7))
+        base = int(r.integers(3 * B, 3 * B + 2400))
+        for _ in range(members):
+            n = base + int(r.integers(-B, B))
+            ctx.append(n)
+            groups.append(c)
+    for _ in range(int(r.integers(0, 3))):
+        ctx.append(int(r.integers(1, 2500)))
+        groups.append(-1)
+    shared = [0] * len(ctx)
+    for c in range(classes):
+        idx = [b for b in range(len(ctx)) if groups[b] == c]
+        room = min((ctx[b] - 1) // B for b in idx)
+        k = int(r.integers(max(1, room // 2), room + 1))
+        for b in idx:
+            shared[b] = k
+    splits = int(r.choice([0, 0, 4, 9, 16]))
+    spec = Spec(f"randpfx{seed}-g{group}x{hkv}-B{B}-b{len(ctx)}", "decode", "bf16", group * hkv,
+                hkv, ctx, [1] * len(ctx), 35_000 + seed, share_group=groups, shared_blocks=shared,
+                block_size=B)
+    return spec, splits
+
+
+@pytest.mark.parametrize("seed", list(range(24)))
+def test_random_prefix_decode_against_oracle(seed):
+    spec, splits = random_prefix_spec(seed)
+    w = build(spec)
+    d = to_device(w)
+    check_inputs(d)
+    S = pkv.pkv_paged_decode_split_tokens(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                          w.max_context_len, w.block_size, splits)
+    plan, items = pkv.pkv_decode_prefix_plan(w.block_tables, w.context_lens, w.num_q_heads,
+                                             w.num_kv_heads, w.block_size, S)
+    assert plan.tolist() == pp.prefix_plan(w.block_tables.tolist(), w.context_lens.tolist(),
+                                           w.block_size, w.num_q_heads // w.num_kv_heads, S)
+    plan = plan.cuda()
+    k_pre, v_pre = d.k_cache.clone(), d.v_cache.clone()
+    announce(f"{spec.name} (splits {splits}, S {S}, {items} items): fused step with plan")
+    out_step = pkv.pkv_paged_decode_step_prefix(
+        d.q, d.k, d.v, d.slot_mapping, d.k_cache, d.v_cache, d.block_tables, d.context_lens,
+        w.max_context_len, w.scale, plan, items, num_splits=splits)
+    torch.cuda.synchronize()
+    kcb, vcb = stored_bits(w)
+    assert np.array_equal(bits_view(d.k_cache.cpu()), kcb)
+    assert np.array_equal(bits_view(d.v_cache.cpu()), vcb)
+    want = expected(w)
+    assert_close(out_step.double().cpu().numpy(), want, f"{spec.name} fused step with plan")
+    d.k_cache.copy_(k_pre)
+    d.v_cache.copy_(v_pre)
+    announce(f"{spec.name}: store, then decode with plan")
+    store(d)
+    out = pkv.pkv_paged_decode_prefix(d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens,
+                                      w.max_context_len, w.scale, plan, items, num_splits=splits)
+    torch.cuda.synchronize()
+    assert_close(out.double().cpu().numpy(), want, f"{spec.name} decode with plan")
+    assert torch.equal(out.view(torch.int16), out_step.view(torch.int16))
