@@ -65,8 +65,12 @@
  * non-decreasing are undefined behaviour.  pkv_last_error() describes the
  * most recent non-OK status of the calling thread.
  *
+ * pkv_check_metadata() checks those contents on the host, for callers that
+ * want such errors reported rather than undefined.
+ *
  * Results are deterministic: a pure function of the inputs and the split
- * plan: every sum runs in a fixed order and no kernel uses atomics.
+ * plan: every sum runs in a fixed order and none uses atomics (the prefill's
+ * work queue does, to hand out work items, which changes no result).
  */
 #ifndef PKV_H_
 #define PKV_H_
@@ -451,6 +455,37 @@ pkv_status pkv_prefill_varlen(
     int32_t max_seqlen_q, int32_t batch, int32_t num_q_heads,
     int32_t num_kv_heads, int32_t head_dim, float scale, int32_t causal,
     void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_check_metadata -- host-side range check of one step's metadata, the
+ * arrays the attention entry points take on the device and never check
+ * (their out-of-range contents are undefined behaviour there; see Errors
+ * above).  A caller that wants such mistakes reported copies the arrays to
+ * the host and calls this before launching.  Every array pointer may be
+ * null: its checks are then skipped.
+ *
+ *   slot_mapping   host int32 [num_tokens]: each -1 or a slot in
+ *                  [0, num_blocks * block_size), no slot twice (the store's
+ *                  contract; architecture page "Prefill- und
+ *                  Decode-Vorbereitung": every stored token has its own slot)
+ *   block_tables   host int32 [batch][max_blocks_per_seq]: the columns
+ *                  context_lens[b] covers hold block ids in [0, num_blocks)
+ *                  (checked only with context_lens)
+ *   context_lens   host int32 [batch]: each in [0, max_context_len] and
+ *                  within max_blocks_per_seq * block_size
+ *   cu_seqlens_q   host int32 [batch + 1]: starts >= 0, non-decreasing, no
+ *                  sequence with more than max_seqlen_q query rows, and
+ *                  cu_seqlens_q[batch] <= total_q (the rows of q; -1: not
+ *                  checked)
+ * Returns PKV_OK, or PKV_ERR_INVALID with pkv_last_error() naming the first
+ * bad entry (array, index, value) or a negative count / size.  Reads only
+ * the given host arrays; no HIP call.
+ */
+pkv_status pkv_check_metadata(const int32_t* slot_mapping, int32_t num_tokens,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, const int32_t* cu_seqlens_q,
+                              int32_t batch, int32_t max_context_len, int32_t max_seqlen_q,
+                              int32_t total_q, int32_t block_size, int64_t num_blocks);
 
 /*
  * pkv_kv_block_bytes -- bytes of one block of one of K or V for one layer

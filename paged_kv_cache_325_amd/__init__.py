@@ -15,7 +15,13 @@ halves ``pkv_paged_decode_partials`` / ``pkv_paged_decode_merge``),
 that plan), ``pkv_paged_decode_workspace_bytes``,
 ``pkv_paged_decode_split_tokens``, ``pkv_paged_prefill_workspace_bytes``,
 ``pkv_paged_prefill_varlen``, ``pkv_prefill_varlen`` (contiguous k/v, no cache),
-``pkv_kv_block_bytes``, ``pkv_last_error``.
+``pkv_kv_block_bytes``, ``pkv_check_metadata``, ``pkv_last_error``.
+
+Debug mode: with the environment variable ``PKV_CHECK_METADATA`` set to a
+value other than ``0``, every call first copies its metadata (slots, block
+tables, context lengths, query offsets) to the host and checks its ranges
+with ``pkv_check_metadata`` (a synchronising copy: not for graph capture or
+timing); out-of-range entries then raise instead of being undefined.
 """
 
 from __future__ import annotations
@@ -36,7 +42,7 @@ __all__ = [
     "pkv_paged_decode_workspace_bytes",
     "pkv_paged_decode_split_tokens", "pkv_paged_prefill_varlen",
     "pkv_paged_prefill_workspace_bytes", "pkv_prefill_varlen", "pkv_kv_block_bytes",
-    "pkv_last_error",
+    "pkv_check_metadata", "pkv_last_error",
 ]
 
 PKV_OK, PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP = range(5)
@@ -115,6 +121,9 @@ def load_library() -> ctypes.CDLL:
                                        ctypes.c_size_t, c_p]
     lib.pkv_paged_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.pkv_paged_prefill_workspace_bytes.argtypes = []
+    lib.pkv_check_metadata.restype = c_i32
+    lib.pkv_check_metadata.argtypes = [c_p, c_i32, c_p, c_i32, c_p, c_p, c_i32, c_i32, c_i32,
+                                       c_i32, c_i32, c_i64]
     lib.pkv_kv_block_bytes.restype = c_i64
     lib.pkv_kv_block_bytes.argtypes = [c_i32, c_i32, c_i32, c_i32]
     lib.pkv_last_error.restype = ctypes.c_char_p
@@ -184,6 +193,44 @@ def pkv_kv_block_bytes(dtype: int, num_kv_heads: int, head_dim: int, block_size:
     return int(load_library().pkv_kv_block_bytes(dtype, num_kv_heads, head_dim, block_size))
 
 
+def pkv_check_metadata(slot_mapping=None, block_tables=None, context_lens=None,
+                       cu_seqlens_q=None, *, max_context_len: int = 0, max_seqlen_q: int = 0,
+                       total_q: int = -1, block_size: int = 256, num_blocks: int = 0) -> None:
+    """Range-check one step's metadata on the host (tensors on any device,
+    or array-likes; copied as int32).  Raises PkvError(PKV_ERR_INVALID)
+    naming the first bad entry; see pkv_check_metadata in include/pkv.h."""
+    def host(a):
+        if a is None:
+            return None
+        t = a.detach() if isinstance(a, torch.Tensor) else torch.as_tensor(a)
+        return t.to("cpu", torch.int32).contiguous()
+    sm, bt, cl, cu = host(slot_mapping), host(block_tables), host(context_lens), host(cu_seqlens_q)
+    if cl is not None:
+        batch = cl.numel()
+    elif cu is not None:
+        batch = max(cu.numel() - 1, 0)
+    else:
+        batch = 0 if bt is None else int(bt.shape[0])
+    max_blocks = 0
+    if bt is not None:
+        if bt.dim() != 2 or bt.shape[0] != batch:
+            raise ValueError("block_tables must be [batch, max_blocks]")
+        max_blocks = int(bt.shape[1])
+    if cu is not None and cu.numel() != batch + 1:
+        raise ValueError("cu_seqlens_q must be [batch + 1]")
+    _check(load_library().pkv_check_metadata(
+        None if sm is None else sm.data_ptr(), 0 if sm is None else sm.numel(),
+        None if bt is None else bt.data_ptr(), max_blocks,
+        None if cl is None else cl.data_ptr(), None if cu is None else cu.data_ptr(), batch,
+        int(max_context_len), int(max_seqlen_q), int(total_q), int(block_size), int(num_blocks)))
+
+
+def _debug_check(**kw) -> None:
+    """pkv_check_metadata(**kw) in debug mode (PKV_CHECK_METADATA set, not 0)."""
+    if os.environ.get("PKV_CHECK_METADATA", "0") not in ("", "0"):
+        pkv_check_metadata(**kw)
+
+
 def pkv_kv_store(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                  slot_mapping: torch.Tensor, stream=None) -> None:
     """Scatter k/v rows ([N, Hkv, D], token stride free) into the caches."""
@@ -199,6 +246,7 @@ def pkv_kv_store(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor, v_cach
     n = k.shape[0]
     if v.shape[0] != n or slot_mapping.numel() != n:
         raise ValueError("k, v and slot_mapping disagree on the number of tokens")
+    _debug_check(slot_mapping=slot_mapping, block_size=bs, num_blocks=nblk)
     _check(lib.pkv_kv_store(_dtype_code(k), _ptr(k), ks, _ptr(v), vs, _ptr(k_cache), _ptr(v_cache),
                             _ptr(slot_mapping), n, hkv, d, bs, nblk, _stream(stream)))
 
@@ -243,6 +291,8 @@ def _decode_call(fn_name, q, k_cache, v_cache, block_tables, context_lens, max_c
     if workspace is None and need > 0:
         workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _debug_check(block_tables=block_tables, context_lens=context_lens,
+                 max_context_len=max_context_len, block_size=bs, num_blocks=nblk)
     _check(getattr(lib, fn_name)(
         _dtype_code(q), _ptr(q), qs, _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), max_blocks,
         _ptr(context_lens), int(max_context_len), batch, hq, hkv, d, bs, nblk, float(scale),
@@ -321,7 +371,7 @@ def pkv_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
 
 
 def _step_args(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables, context_lens,
-               out):
+               out, max_context_len):
     """Checked pointers and sizes of a decode step (shared by both forms)."""
     for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"),
                  (v_cache, "v_cache")):
@@ -346,6 +396,8 @@ def _step_args(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables, co
     _gpu(out, "out")
     if out.shape != (batch, hq, d) or not out.is_contiguous() or out.dtype != q.dtype:
         raise ValueError("out must be a contiguous [batch, Hq, D] tensor of q's dtype")
+    _debug_check(slot_mapping=slot_mapping, block_tables=block_tables, context_lens=context_lens,
+                 max_context_len=max_context_len, block_size=bs, num_blocks=nblk)
     return (batch, hq, hkv, d, bs, nblk,
             [_dtype_code(q), _ptr(q), qs, _ptr(k_new), ks, _ptr(v_new), vs, _ptr(slot_mapping),
              _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), int(block_tables.shape[1]),
@@ -366,7 +418,8 @@ def pkv_paged_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Ten
         _gpu(q, "q")
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     batch, hq, hkv, d, bs, nblk, head = _step_args(q, k_new, v_new, slot_mapping, k_cache,
-                                                   v_cache, block_tables, context_lens, out)
+                                                   v_cache, block_tables, context_lens, out,
+                                                   max_context_len)
     need = pkv_paged_decode_workspace_bytes(batch, hq, hkv, d, max_context_len, bs, num_splits)
     if workspace is None and need > 0:
         workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
@@ -392,7 +445,8 @@ def pkv_paged_decode_step_prefix(q: torch.Tensor, k_new: torch.Tensor, v_new: to
         _gpu(q, "q")
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     batch, hq, hkv, d, bs, nblk, head = _step_args(q, k_new, v_new, slot_mapping, k_cache,
-                                                   v_cache, block_tables, context_lens, out)
+                                                   v_cache, block_tables, context_lens, out,
+                                                   max_context_len)
     need = pkv_paged_decode_workspace_bytes(batch, hq, hkv, d, max_context_len, bs, num_splits)
     if workspace is None and need > 0:
         workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
@@ -416,7 +470,8 @@ def pkv_paged_decode_step_noalloc(q: torch.Tensor, k_new: torch.Tensor, v_new: t
     one GPU race on the scratch."""
     lib = load_library()
     batch, hq, hkv, d, bs, nblk, head = _step_args(q, k_new, v_new, slot_mapping, k_cache,
-                                                   v_cache, block_tables, context_lens, out)
+                                                   v_cache, block_tables, context_lens, out,
+                                                   max_context_len)
     _check(lib.pkv_paged_decode_step_noalloc(
         *head, int(max_context_len), batch, hq, hkv, d, bs, nblk, float(scale),
         int(num_splits), _ptr(out), _stream(stream)))
@@ -498,6 +553,9 @@ def pkv_paged_prefill_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: to
         workspace = _prefill_workspace(q.device, st)
     _gpu(workspace, "workspace")
     ws_bytes = workspace.numel() * workspace.element_size()
+    _debug_check(block_tables=block_tables, context_lens=context_lens, cu_seqlens_q=cu_seqlens_q,
+                 max_context_len=max_context_len, max_seqlen_q=max_seqlen_q, total_q=total,
+                 block_size=bs, num_blocks=nblk)
     _check(lib.pkv_paged_prefill_varlen(_dtype_code(q), _ptr(q), qs, _ptr(k_cache), _ptr(v_cache),
                                         _ptr(cu_seqlens_q), int(max_seqlen_q), _ptr(context_lens),
                                         int(max_context_len), _ptr(block_tables),
@@ -541,6 +599,9 @@ def pkv_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         workspace = _prefill_workspace(q.device, st)
     _gpu(workspace, "workspace")
     ws_bytes = workspace.numel() * workspace.element_size()
+    # query offsets against q's rows, key offsets against k's rows
+    _debug_check(cu_seqlens_q=cu_seqlens_q, max_seqlen_q=max_seqlen_q, total_q=total)
+    _debug_check(cu_seqlens_q=cu_seqlens_k, max_seqlen_q=int(k.shape[0]), total_q=int(k.shape[0]))
     _check(lib.pkv_prefill_varlen(_dtype_code(q), _ptr(q), qs, _ptr(k), ks, _ptr(v), vs,
                                   _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), int(max_seqlen_q), batch,
                                   hq, hkv, d, float(scale), int(causal), _ptr(out),
