@@ -213,10 +213,28 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4
   const int b = id % a.batch;
   const int r = id / a.batch;  // workgroup tile counted from the end
 
-  const int q_begin = a.cu_q[b];
-  const int n_q = a.cu_q[b + 1] - q_begin;
-  const int k_begin = a.cu_k ? a.cu_k[b] : 0;
-  const int n_k = a.cu_k ? a.cu_k[b + 1] - k_begin : a.ctx[b];
+  // Block-table entries of the item, loaded once: lane i holds logical
+  // blocks i and 64 + i; beyond 128 blocks a scalar load (constant address
+  // space) is used.  A per-tile global load would make the copy wait on
+  // every vector memory access in flight, including the copies of the
+  // previous tiles.  The row's first 128 columns are loaded whether the
+  // item uses them or not (all inside the table), before the sequence's
+  // lengths are known, so that the two loads share one memory round trip.
+  const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
+  const int tcols = (a.cu_k || !a.block_tables) ? 0 : min(a.max_blocks, 128);
+  const int32_t tab0 = lane < tcols ? table[lane] : 0;
+  const int32_t tab1 = lane + 64 < tcols ? table[lane + 64] : 0;
+
+  // The sequence's lengths: uniform over the workgroup and read-only for the
+  // launch, so scalar loads (constant address space) through the scalar
+  // cache, which every item of the launch shares; as plain loads they were
+  // vector loads, each waited for in turn.
+  typedef const __attribute__((address_space(4))) int32_t const_i32;
+  auto sload = [](const int32_t* p, int i) { return ((const_i32*)p)[i]; };
+  const int q_begin = sload(a.cu_q, b);
+  const int n_q = sload(a.cu_q, b + 1) - q_begin;
+  const int k_begin = a.cu_k ? sload(a.cu_k, b) : 0;
+  const int n_k = a.cu_k ? sload(a.cu_k, b + 1) - k_begin : sload(a.ctx, b);
   const int off = n_k - n_q;
   const int wg_rows = kQT * a.pos_tiles;
   const int wg_tiles = (n_q + wg_rows - 1) / wg_rows;
@@ -254,12 +272,6 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4
   float l_part = 0.f;
   const float c = a.scale_log2;
 
-  // Block-table entries of the item, loaded once: lane i holds logical
-  // blocks i and 64 + i; beyond 128 blocks a scalar load (constant address
-  // space) is used.  A per-tile global load would make the copy wait on
-  // every vector memory access in flight, including the copies of the
-  // previous tiles.
-  const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
   constexpr bool kSmall = kBlock < 0;
   const uint32_t bs = kBlock > 0 ? (uint32_t)kBlock : a.bdiv.d;
   auto block_of = [&](uint32_t key) -> uint32_t {
@@ -267,9 +279,6 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int id, u32x4
     else if constexpr (kSmall) return key >> (bs == 16 ? 4 : 5);
     else return a.bdiv.div(key);
   };
-  const int nblk = a.cu_k ? 0 : (int)block_of((uint32_t)(wg_kend + bs - 1));
-  const int32_t tab0 = lane < nblk ? table[lane] : 0;
-  const int32_t tab1 = lane + 64 < nblk ? table[lane + 64] : 0;
   auto block_at = [&](int i) -> int64_t {  // i uniform
     if (i < 64) return __builtin_amdgcn_readlane(tab0, i);
     if (i < 128) return __builtin_amdgcn_readlane(tab1, i - 64);
