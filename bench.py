@@ -455,8 +455,8 @@ TRAFFIC = {
         "bytes": 9229820, "source": "decode.hip",
         "sha256": "5ee831548692cf55da7dd9962dbcd5155c713c0c1c859ffccb8694cad34015c9"},
     ("prefill_kernel", "prefill-bf16-8seq-L1024-4096-prefix512-h32-8"): {
-        "bytes": 2068378548, "source": "prefill.hip",
-        "sha256": "5b1786f6a5dfd25ce2425141c2bf9c994e178782b8660d8820a87f226612c4db"},
+        "bytes": 2074232850, "source": "prefill.hip",
+        "sha256": "d6349ec4a18e79c3d90a65b94067f1dc170db6e80ffbbb8c5952a5a2f1cd7029"},
 }
 
 
