@@ -618,7 +618,9 @@ pkv_status pkv_prefill_varlen(pkv_dtype dtype, const void* q, int64_t q_token_st
   l.v_cache = nullptr;
   l.cu_seqlens_q = cu_seqlens_q;
   l.max_seqlen_q = max_seqlen_q;
-  l.context_lens = nullptr;
+  // not read when the keys come from cu_seqlens_k, but a valid array all the
+  // same (batch + 1 entries), so that no load through it could fault
+  l.context_lens = cu_seqlens_k;
   l.block_tables = nullptr;
   l.max_blocks = 0;
   l.batch = batch;
