@@ -619,7 +619,8 @@ def summary(r) -> dict:
 
 def host_cores() -> int:
     """CPU threads this process may use: its affinity set, capped by
-    OMP_NUM_THREADS when that is set (a GPU machine grants a share of its host)."""
+    OMP_NUM_THREADS when that is set (a shared host may grant only a share of
+    its cores through it)."""
     n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     omp = os.environ.get("OMP_NUM_THREADS", "")
     return min(n, int(omp)) if omp.isdigit() and int(omp) > 0 else n
