@@ -828,31 +828,38 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
-// Merge the split partials of one (sequence, query head) per wavefront:
-// M = max_s m_s, out = sum_s 2^(m_s-M) acc_s / sum_s 2^(m_s-M) l_s, with the
-// acc sum taken in split order.  The kernel is latency-bound (a few KB per
-// wavefront), so every load is issued before the first use: lane s fetches
-// split s's (m, l), and the acc rows of a batch of splits (4 or 16) are in
-// flight while the maximum is reduced.  Splits beyond 64 (very long
-// contexts with small splits) go through the general loop.  Sequences with
-// a single split were finished by the split kernel.
+// Merge the split partials of one (sequence, query head):
+// M = max_s m_s, out = sum_s 2^(m_s-M) acc_s / sum_s 2^(m_s-M) l_s.  The
+// kernel is latency-bound (a few KB per pair), so every load is issued
+// before the first use: lane s fetches split s's (m, l), and the acc rows of
+// a batch of splits (4 or 16) are in flight while the maximum is reduced.
+// Splits beyond 64 (very long contexts with small splits) go through the
+// general loop.  Sequences with a single split were finished by the split
+// kernel.
 //
-// merge_pair: one (sequence, query head) pair with ns splits, acc rows read
+// merge_pair: one pair with ns splits on kWaves wavefronts, acc rows read
 // kBatch at a time (rows past the end are re-reads of the last row, with
-// weight 0).
-template <int kElemBytes, int kBatch>
-__device__ __forceinline__ void merge_pair(const DecodeArgs& a, int pair, int ns) {
+// weight 0).  With one wavefront the acc sum is taken in split order.  With
+// four (kBatch 16), wave w sums rows 16w .. 16w+15 of every group of 64
+// splits in split order, and the four partial sums are added in wave order
+// through `red`: one round of loads per group instead of four.
+template <int kElemBytes, int kBatch, int kWaves = 1>
+__device__ __forceinline__ void merge_pair(const DecodeArgs& a, int pair, int ns,
+                                           f32x2 (*red)[64] = nullptr) {
+  static_assert(kWaves == 1 || kWaves * kBatch == 64, "a group of 64 splits per round");
   const int lane = threadIdx.x & 63;
+  const int wave = kWaves == 1 ? 0 : (int)(threadIdx.x >> 6);
+  const int r0 = wave * kBatch;  // this wave's first row within each group
   const int64_t base = (int64_t)pair * a.nsplit;
   const float* acc_rows = a.ws_acc + base * kHeadDim + lane * 2;
 
-  // first group: (m, l) of splits 0..63 and acc rows of splits 0..kBatch-1
+  // first group: (m, l) of splits 0..63 and this wave's first batch of acc rows
   f32x2 ml = f32x2{-INFINITY, 0.f};
   if (lane < ns) ml = *reinterpret_cast<const f32x2*>(a.ws_ml + (base + lane) * 2);
   f32x2 v[kBatch];
 #pragma unroll
   for (int j = 0; j < kBatch; ++j)
-    v[j] = *reinterpret_cast<const f32x2*>(acc_rows + (int64_t)min(j, ns - 1) * kHeadDim);
+    v[j] = *reinterpret_cast<const f32x2*>(acc_rows + (int64_t)min(r0 + j, ns - 1) * kHeadDim);
 
   float M = ml[0];
   for (int g0 = 64; g0 < ns; g0 += 64) {
@@ -871,8 +878,8 @@ __device__ __forceinline__ void merge_pair(const DecodeArgs& a, int pair, int ns
     const float f = fast_exp2(ml[0] - M);  // 0 for lanes past the end
     l_lane = fmaf(f, ml[1], l_lane);
     const int gn = min(64, ns - g0);
-    for (int j0 = 0; j0 < gn; j0 += kBatch) {
-      if (g0 > 0 || j0 > 0) {
+    for (int j0 = r0; j0 < gn; j0 += kBatch * kWaves) {
+      if (g0 > 0 || j0 > r0) {
 #pragma unroll
         for (int j = 0; j < kBatch; ++j)
           v[j] = *reinterpret_cast<const f32x2*>(
@@ -884,6 +891,18 @@ __device__ __forceinline__ void merge_pair(const DecodeArgs& a, int pair, int ns
         o0 = fmaf(fj, v[j][0], o0);
         o1 = fmaf(fj, v[j][1], o1);
       }
+    }
+  }
+  if constexpr (kWaves > 1) {
+    red[wave][lane] = f32x2{o0, o1};
+    __syncthreads();
+    if (wave != 0) return;
+    o0 = red[0][lane][0];
+    o1 = red[0][lane][1];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      o0 += red[w][lane][0];
+      o1 += red[w][lane][1];
     }
   }
   const float inv = 1.0f / wave_sum(l_lane);
@@ -901,7 +920,8 @@ __device__ __forceinline__ void merge_pair(const DecodeArgs& a, int pair, int ns
 // plan has 1-4 per sequence) take a 4-row batch: the load instructions of
 // the 16-row batch (12 of them re-reads) were what bounded that merge
 // (11.9 -> 8.6 us, bitwise equal; a path per power of two up to 32 cost
-// registers and occupancy and was slower).
+// registers and occupancy and was slower).  Four pairs per workgroup, one
+// per wavefront.
 template <int kElemBytes>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -914,6 +934,30 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     merge_pair<kElemBytes, 4>(a, pair, ns);
   else
     merge_pair<kElemBytes, 16>(a, pair, ns);
+}
+
+// Plans with more than 16 splits: one pair per workgroup.  A pair with more
+// than 16 splits is merged by all four wavefronts (see merge_pair); one with
+// fewer by the first wavefront alone, exactly as decode_merge_kernel does.
+// (The branches depend only on the pair, i.e. on the workgroup, so every
+// wavefront of a workgroup reaches the barrier in merge_pair or none does.)
+template <int kElemBytes>
+__global__ __launch_bounds__(256) void decode_merge_wide_kernel(DecodeArgs a) {
+  __shared__ f32x2 red[4][64];
+  const int pair = blockIdx.x;
+  const int b = pair / a.num_q_heads;
+  const int n = a.context_lens[b];
+  const int ns = (n + a.split_tokens - 1) / a.split_tokens;
+  if (ns <= 1) return;
+  if (ns <= 16) {
+    if (threadIdx.x >= 64) return;
+    if (ns <= 4)
+      merge_pair<kElemBytes, 4>(a, pair, ns);
+    else
+      merge_pair<kElemBytes, 16>(a, pair, ns);
+    return;
+  }
+  merge_pair<kElemBytes, 16, 4>(a, pair, ns, red);
 }
 
 template <int kElemBytes, int kHeads, bool kSmall>
@@ -1074,6 +1118,14 @@ hipError_t launch_decode_merge(int elem_bytes, const DecodePlan& plan, const Dec
   if (plan.nsplit <= 1 || l.batch <= 0) return hipSuccess;  // nothing was split
   const DecodeArgs a = decode_args(elem_bytes, plan, l);
   const int64_t pairs = (int64_t)l.batch * l.num_q_heads;
+  if (plan.nsplit > 16) {
+    if (pairs > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (elem_bytes == 2)
+      hipLaunchKernelGGL(decode_merge_wide_kernel<2>, dim3((unsigned)pairs), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(decode_merge_wide_kernel<4>, dim3((unsigned)pairs), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   const unsigned mgrid = (unsigned)((pairs + 3) / 4);
   if (elem_bytes == 2)
     hipLaunchKernelGGL(decode_merge_kernel<2>, dim3(mgrid), dim3(256), 0, stream, a);

@@ -193,12 +193,17 @@ def test_split_partials_in_workspace():
     assert_close(out2.double().cpu().numpy(), expected(w), "reused workspace")
 
 
-def test_merge_of_oracle_partials():
+# 5 requested splits: 1-5 per sequence (the merge's one-wavefront forms);
+# 24: splits of 256 keys, 12-20 per long sequence (the plan has more than 16,
+# so the four-wavefront merge runs, and takes the one-wavefront form for the
+# sequence with 12); 100: splits of 64 keys, up to 79 (more than one group of
+# 64 splits in the four-wavefront form).
+@pytest.mark.parametrize("splits", [5, 24, 100])
+def test_merge_of_oracle_partials(splits):
     """The merge entry point alone: fed the oracle's split partials (written
     into the documented workspace layout), it must produce the oracle's
     merged output."""
     w = build([s for s in SMALL if s.name == "dec-bf16-g4-long"][0])
-    splits = 5
     args = (w.batch, w.num_q_heads, w.num_kv_heads, 128, w.max_context_len, 256, splits)
     S = pkv.pkv_paged_decode_split_tokens(*args)
     ns = -(-w.max_context_len // S)
@@ -227,7 +232,7 @@ def test_merge_of_oracle_partials():
     ws = torch.from_numpy(host).cuda()
     out = torch.full((w.batch, w.num_q_heads, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
     ctx = torch.from_numpy(w.context_lens).cuda()
-    announce("merge of oracle partials")
+    announce(f"merge of oracle partials, {ns} splits")
     pkv.pkv_paged_decode_merge(ctx, w.max_context_len, w.num_q_heads, w.num_kv_heads,
                                w.block_size, out, ws,
                                num_splits=splits)
