@@ -828,38 +828,38 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
-// Merge the split partials of one (sequence, query head):
-// M = max_s m_s, out = sum_s 2^(m_s-M) acc_s / sum_s 2^(m_s-M) l_s.  The
-// kernel is latency-bound (a few KB per pair), so every load is issued
-// before the first use: lane s fetches split s's (m, l), and the acc rows of
-// a batch of splits (4 or 16) are in flight while the maximum is reduced.
-// Splits beyond 64 (very long contexts with small splits) go through the
-// general loop.  Sequences with a single split were finished by the split
-// kernel.
+// Merge the split partials of one (sequence, query head) per wavefront:
+// M = max_s m_s, out = sum_s 2^(m_s-M) acc_s / sum_s 2^(m_s-M) l_s, with the
+// acc sum taken in split order.  The kernel is latency-bound (a few KB per
+// wavefront), so every load is issued before the first use: lane s fetches
+// split s's (m, l), and the acc rows of a batch of splits (4 or 16) are in
+// flight while the maximum is reduced.  Splits beyond 64 (very long
+// contexts with small splits) go through the general loop.  Sequences with
+// a single split were finished by the split kernel.
 //
-// merge_pair: one pair with ns splits on kWaves wavefronts, acc rows read
+// merge_pair: one (sequence, query head) pair with ns splits, acc rows read
 // kBatch at a time (rows past the end are re-reads of the last row, with
-// weight 0).  With one wavefront the acc sum is taken in split order.  With
-// four (kBatch 16), wave w sums rows 16w .. 16w+15 of every group of 64
-// splits in split order, and the four partial sums are added in wave order
-// through `red`: one round of loads per group instead of four.
-template <int kElemBytes, int kBatch, int kWaves = 1>
+// weight 0).  kStaged (kBatch 16; decode_merge_wide_kernel): rows 16..63 of
+// each group of 64 splits are not loaded here but taken from `stage`, where
+// wavefronts 1-3 of the workgroup load them (merge_stage_rows) while this
+// one loads rows 0..15 -- one round of loads per group instead of four, and
+// the same arithmetic in the same order, so bitwise the same result.  Both
+// sides pass two barriers per group: rows staged, stage free again.
+template <int kElemBytes, int kBatch, bool kStaged = false>
 __device__ __forceinline__ void merge_pair(const DecodeArgs& a, int pair, int ns,
-                                           f32x2 (*red)[64] = nullptr) {
-  static_assert(kWaves == 1 || kWaves * kBatch == 64, "a group of 64 splits per round");
+                                           const f32x2 (*stage)[64] = nullptr) {
+  static_assert(!kStaged || kBatch == 16, "staged rows come in batches of 16");
   const int lane = threadIdx.x & 63;
-  const int wave = kWaves == 1 ? 0 : (int)(threadIdx.x >> 6);
-  const int r0 = wave * kBatch;  // this wave's first row within each group
   const int64_t base = (int64_t)pair * a.nsplit;
   const float* acc_rows = a.ws_acc + base * kHeadDim + lane * 2;
 
-  // first group: (m, l) of splits 0..63 and this wave's first batch of acc rows
+  // first group: (m, l) of splits 0..63 and acc rows of splits 0..kBatch-1
   f32x2 ml = f32x2{-INFINITY, 0.f};
   if (lane < ns) ml = *reinterpret_cast<const f32x2*>(a.ws_ml + (base + lane) * 2);
   f32x2 v[kBatch];
 #pragma unroll
   for (int j = 0; j < kBatch; ++j)
-    v[j] = *reinterpret_cast<const f32x2*>(acc_rows + (int64_t)min(r0 + j, ns - 1) * kHeadDim);
+    v[j] = *reinterpret_cast<const f32x2*>(acc_rows + (int64_t)min(j, ns - 1) * kHeadDim);
 
   float M = ml[0];
   for (int g0 = 64; g0 < ns; g0 += 64) {
@@ -878,8 +878,12 @@ __device__ __forceinline__ void merge_pair(const DecodeArgs& a, int pair, int ns
     const float f = fast_exp2(ml[0] - M);  // 0 for lanes past the end
     l_lane = fmaf(f, ml[1], l_lane);
     const int gn = min(64, ns - g0);
-    for (int j0 = r0; j0 < gn; j0 += kBatch * kWaves) {
-      if (g0 > 0 || j0 > r0) {
+    if constexpr (kStaged) __syncthreads();  // this group's rows 16.. staged
+    for (int j0 = 0; j0 < gn; j0 += kBatch) {
+      if (kStaged && j0 > 0) {
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) v[j] = stage[j0 - 16 + j][lane];
+      } else if (g0 > 0 || j0 > 0) {
 #pragma unroll
         for (int j = 0; j < kBatch; ++j)
           v[j] = *reinterpret_cast<const f32x2*>(
@@ -892,18 +896,7 @@ __device__ __forceinline__ void merge_pair(const DecodeArgs& a, int pair, int ns
         o1 = fmaf(fj, v[j][1], o1);
       }
     }
-  }
-  if constexpr (kWaves > 1) {
-    red[wave][lane] = f32x2{o0, o1};
-    __syncthreads();
-    if (wave != 0) return;
-    o0 = red[0][lane][0];
-    o1 = red[0][lane][1];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) {
-      o0 += red[w][lane][0];
-      o1 += red[w][lane][1];
-    }
+    if constexpr (kStaged) __syncthreads();  // stage free for the next group
   }
   const float inv = 1.0f / wave_sum(l_lane);
   constexpr int kRowBytes = kHeadDim * kElemBytes;
@@ -913,6 +906,31 @@ __device__ __forceinline__ void merge_pair(const DecodeArgs& a, int pair, int ns
   } else {
     *reinterpret_cast<f32x2*>(a.out + (int64_t)pair * kRowBytes + lane * 8) =
         f32x2{o0 * inv, o1 * inv};
+  }
+}
+
+// Wavefront w = 1..3 of a decode_merge_wide_kernel workgroup: for each group
+// of 64 splits, load acc rows 16w..16w+15 (clamped to the group's last row,
+// as merge_pair would) into stage[16(w-1)..], then wait while wavefront 0
+// consumes them.
+__device__ __forceinline__ void merge_stage_rows(const DecodeArgs& a, int pair, int ns,
+                                                 f32x2 (*stage)[64]) {
+  const int lane = threadIdx.x & 63;
+  const int r0 = (int)(threadIdx.x >> 6) * 16;
+  const float* acc_rows = a.ws_acc + (int64_t)pair * a.nsplit * kHeadDim + lane * 2;
+  for (int g0 = 0; g0 < ns; g0 += 64) {
+    const int gn = min(64, ns - g0);
+    if (r0 < gn) {
+      f32x2 v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        v[j] = *reinterpret_cast<const f32x2*>(
+            acc_rows + (int64_t)(g0 + min(r0 + j, gn - 1)) * kHeadDim);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) stage[r0 - 16 + j][lane] = v[j];
+    }
+    __syncthreads();  // rows staged
+    __syncthreads();  // wavefront 0 has read them
   }
 }
 
@@ -936,14 +954,15 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     merge_pair<kElemBytes, 16>(a, pair, ns);
 }
 
-// Plans with more than 16 splits: one pair per workgroup.  A pair with more
-// than 16 splits is merged by all four wavefronts (see merge_pair); one with
-// fewer by the first wavefront alone, exactly as decode_merge_kernel does.
-// (The branches depend only on the pair, i.e. on the workgroup, so every
-// wavefront of a workgroup reaches the barrier in merge_pair or none does.)
+// Plans with more than 16 splits: one pair per workgroup of four
+// wavefronts.  A pair with more than 16 splits is merged by wavefront 0
+// with wavefronts 1-3 loading its acc rows (see merge_pair); one with fewer
+// by wavefront 0 alone, exactly as decode_merge_kernel does.  (The branches
+// depend only on the pair, i.e. on the workgroup, so every wavefront of a
+// workgroup passes the same barriers or none.)
 template <int kElemBytes>
 __global__ __launch_bounds__(256) void decode_merge_wide_kernel(DecodeArgs a) {
-  __shared__ f32x2 red[4][64];
+  __shared__ f32x2 stage[48][64];
   const int pair = blockIdx.x;
   const int b = pair / a.num_q_heads;
   const int n = a.context_lens[b];
@@ -957,7 +976,10 @@ __global__ __launch_bounds__(256) void decode_merge_wide_kernel(DecodeArgs a) {
       merge_pair<kElemBytes, 16>(a, pair, ns);
     return;
   }
-  merge_pair<kElemBytes, 16, 4>(a, pair, ns, red);
+  if (threadIdx.x < 64)
+    merge_pair<kElemBytes, 16, true>(a, pair, ns, stage);
+  else
+    merge_stage_rows(a, pair, ns, stage);
 }
 
 template <int kElemBytes, int kHeads, bool kSmall>
