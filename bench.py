@@ -443,17 +443,17 @@ def time_layer_stack(torch, w, layers: int = 28, reps: int = 20) -> dict:
 # changes, the figure no longer describes the kernel and is reported as null.
 TRAFFIC = {
     ("decode_split_kernel", "decode-bf16-b256-ctx1024-8192-h32-8"): {
-        "bytes": 4844620560, "source": "decode.hip",
-        "sha256": "5d7c77a943f49633a4944ef7814d48c21aba911cbe697e67055e446953565a38"},
+        "bytes": 4844618811, "source": "decode.hip",
+        "sha256": "b64697fe84a19af58d02c3e4a18983fbb38da73e634959b6f57779efacce1407"},
     ("decode_split_kernel", "decode-bf16-b64-ctx512-4096-h16-8"): {
-        "bytes": 545475697, "source": "decode.hip",
-        "sha256": "5d7c77a943f49633a4944ef7814d48c21aba911cbe697e67055e446953565a38"},
+        "bytes": 545483092, "source": "decode.hip",
+        "sha256": "b64697fe84a19af58d02c3e4a18983fbb38da73e634959b6f57779efacce1407"},
     ("decode_split_kernel", "decode-bf16-b16-lognormal8192-shared4096-h32-8"): {
-        "bytes": 615835890, "source": "decode.hip",
-        "sha256": "5d7c77a943f49633a4944ef7814d48c21aba911cbe697e67055e446953565a38"},
+        "bytes": 616375385, "source": "decode.hip",
+        "sha256": "b64697fe84a19af58d02c3e4a18983fbb38da73e634959b6f57779efacce1407"},
     ("decode_split_kernel", "decode-fp32-4seq"): {
-        "bytes": 9229914, "source": "decode.hip",
-        "sha256": "5d7c77a943f49633a4944ef7814d48c21aba911cbe697e67055e446953565a38"},
+        "bytes": 9229930, "source": "decode.hip",
+        "sha256": "b64697fe84a19af58d02c3e4a18983fbb38da73e634959b6f57779efacce1407"},
     ("prefill_kernel", "prefill-bf16-8seq-L1024-4096-prefix512-h32-8"): {
         "bytes": 2074232850, "source": "prefill.hip",
         "sha256": "d6349ec4a18e79c3d90a65b94067f1dc170db6e80ffbbb8c5952a5a2f1cd7029"},
