@@ -244,6 +244,61 @@ def test_merge_of_oracle_partials(splits):
     assert torch.isnan(out[others].float()).all()
 
 
+def _bf16_rne_bits(x: np.ndarray) -> np.ndarray:
+    """Bits of float32 values rounded to bfloat16, to nearest even (finite
+    values only)."""
+    u = x.astype(np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+# Partials with every m_s = 0 and l_s = 1: each weight 2^(m_s - M) is 1
+# exactly and the denominator is the split count, a power of two, so the
+# merged row is exactly bf16(fp32 sum of acc_s taken in split order / ns).
+# Each acc element is +-2^20 (signs balanced over the splits, in a random
+# order) plus a standard normal: the running sum's rounding then depends on
+# the order of the additions far beyond bf16's resolution of the result
+# (on the CPU, summing these rows in reverse order changes 46-98 % of the
+# bf16 outputs of each sequence, and as four interleaved partial sums of 16
+# rows per group, 88-97 % of those with more than 16 splits).  16 requested
+# splits: 16/8/4 per sequence (the one-wavefront merge kernel); 64: 64/32/16
+# (the four-wavefront kernel, staged and not); 128: 128/64/32 (two groups
+# of 64).
+@pytest.mark.parametrize("splits", [16, 64, 128])
+def test_merge_sums_in_split_order_bitwise(splits):
+    batch, hq, hkv, max_ctx = 3, 8, 2, 16384
+    ctx = np.array([16384, 8192, 4096], np.int32)
+    S = pkv.pkv_paged_decode_split_tokens(batch, hq, hkv, 128, max_ctx, 256, splits)
+    nsplit = -(-max_ctx // S)
+    assert nsplit == splits
+    r = np.random.default_rng(31_000 + splits)
+    acc = r.standard_normal((batch, hq, nsplit, 128)).astype(np.float32)
+    for b in range(batch):
+        ns = -(-int(ctx[b]) // S)
+        signs = np.where(np.arange(ns) % 2 == 0, 1.0, -1.0)
+        big = np.stack([np.stack([r.permutation(signs) for _ in range(128)], -1)
+                        for _ in range(hq)], 0)  # [hq, ns, 128]
+        acc[b, :, :ns] += (big * 2.0 ** 20).astype(np.float32)
+    ml = np.zeros((batch, hq, nsplit, 2), np.float32)
+    ml[..., 1] = 1.0
+    host = np.concatenate([acc.ravel(), ml.ravel()])
+    assert host.size * 4 == pkv.pkv_paged_decode_workspace_bytes(batch, hq, hkv, 128, max_ctx,
+                                                                 256, splits)
+    ws = torch.from_numpy(host).cuda()
+    out = torch.zeros((batch, hq, 128), dtype=torch.bfloat16, device="cuda")
+    announce(f"merge in split order, {splits} splits")
+    pkv.pkv_paged_decode_merge(torch.from_numpy(ctx).cuda(), max_ctx, hq, hkv, 256, out, ws,
+                               num_splits=splits)
+    torch.cuda.synchronize()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    for b in range(batch):
+        ns = -(-int(ctx[b]) // S)
+        total = np.zeros((hq, 128), np.float32)
+        for sp in range(ns):
+            total = (total + acc[b, :, sp]).astype(np.float32)
+        want = _bf16_rne_bits(total * np.float32(1.0 / ns))
+        assert np.array_equal(got[b], want), (b, ns)
+
+
 def test_partials_then_merge_equals_decode_bit_exact():
     w = build([s for s in SMALL if s.name == "dec-bf16-g2-ragged"][0])
     d = to_device(w)
