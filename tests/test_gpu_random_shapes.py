@@ -78,7 +78,7 @@ def random_spec(seed: int) -> tuple[Spec, int]:
         scale = float(r.uniform(0.2, 0.5))
     q_scale = 4.0 if r.random() < 0.15 else 1.0
     pad = int(r.integers(0, 3))
-    splits = int(r.choice([0, 0, 1, 2, 3, 5, 8])) if mode == "decode" else 0
+    splits = int(r.choice([0, 0, 1, 2, 3, 5, 8, 24, 40])) if mode == "decode" else 0
     # an all-empty batch still gets a (poisoned) one-block cache: a cache of
     # no blocks has no storage, and the library refuses a null cache with
     # token rows to store (even rows whose slot is -1)
